@@ -1,0 +1,192 @@
+/*
+ * sdpa.h -- C ABI of libsdpa.so: fused scaled dot-product attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ *     O = softmax(scale * Q K^T + M) V
+ *
+ * computed tile by tile with an online softmax, so the [B, Hq, Lq, Lk]
+ * score tensor is never stored.  Definition and sources:
+ *   - mlx issue "mx.fast.scaled_dot_product_attention produces incorrect
+ *     attention scores (MLX 0.31.2)", section "Reproduction": the manual
+ *     attention (Q K^T times scale, softmax over the key axis, times V) that
+ *     the fused operation must equal;  same page, root-cause comment: the
+ *     kernel addresses Q, K, V through explicit batch / head / sequence
+ *     strides, and reading a [B,L,H,D] tensor as if it were [B,H,L,D] is the
+ *     bug that page reports.  This ABI therefore takes every dimension as an
+ *     explicit argument and every tensor with its own logical strides; it
+ *     never infers a shape from memory order.
+ *   - mlx issue #3885 "Metal SDPA: no fused path for head_dim=512 (vector or
+ *     full kernel), and the fallback is silent": queries of length <= 8 take
+ *     the "vector" (decode) kernel, longer ones the "full" (prefill) kernel;
+ *     grouped-query heads (scores [B, n_kv, n_rep, qL, kL]); a silent
+ *     unfused fallback is the failure to avoid, and a queryable predicate
+ *     plus a once-per-shape route log are the remedies asked for.
+ *   - mlx PR #4330 "Support head dimension 72 in Metal full attention":
+ *     mask kinds none / additive / boolean / causal, aligned and unaligned
+ *     lengths, float16 / bfloat16 / float32.
+ *   - mlxcel issue #1065 "f32 matmul and single-query SDPA lose ~fp16
+ *     precision on M5": float32 inputs must be computed in float32.
+ *
+ * Conventions shared by every entry point
+ *   - Shapes are logical: Q [B, Hq, Lq, D], K and V [B, Hkv, Lk, D],
+ *     O [B, Hq, Lq, D], mask broadcastable to [B, Hq, Lq, Lk].
+ *   - Strides are in ELEMENTS, in logical (b, h, l, d) order.  A [B,L,H,D]
+ *     tensor has strides (L*H*D, D, H*D, 1); a [B,H,L,D] one (H*L*D, L*D, D, 1).
+ *     The d stride must be 1.  For Q, K, V and O every other stride and the
+ *     base address must be 16-byte aligned (a multiple of 8 elements for
+ *     16-bit types, 4 for float32).
+ *   - Grouped-query attention: Hq must be a multiple of Hkv; query head h
+ *     reads key/value head h / (Hq / Hkv).
+ *   - Device pointers are HIP device pointers on the current device; the
+ *     caller owns every buffer (including the workspace) and must keep it
+ *     alive until `stream` has executed the call.  The library allocates
+ *     nothing on this path and keeps no pointer after returning.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; errors from kernels that already ran
+ *     surface on a later HIP call, as for any HIP launch.
+ *   - Every argument is checked before anything is enqueued: on any error
+ *     nothing is written.  No entry point aborts, throws or prints (except
+ *     the opt-in route log, SDPA_LOG_ROUTE=1, to stderr).
+ */
+#ifndef SDPA_H
+#define SDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  SDPA_U8 is only valid as the element type of a boolean mask. */
+typedef enum { SDPA_F32 = 0, SDPA_F16 = 1, SDPA_BF16 = 2, SDPA_U8 = 3 } sdpa_dtype;
+
+/* Mask kinds (mlx PR #4330, "Proposed changes": unmasked, additive, boolean, causal).
+ *   NONE      M = 0.
+ *   ADDITIVE  M[b,h,i,j] = stored value (element type = dtype or SDPA_F32), added
+ *             after the scale, not scaled.  -inf entries are allowed.
+ *   BOOLEAN   one byte per element: nonzero = attend (M = 0), zero = masked (M = -inf).
+ *   CAUSAL    no tensor; bottom-right aligned: query i attends key j iff
+ *             j <= i + (Lk - Lq).
+ * Mask strides use the same logical (b, h, l, d) order with `d` meaning the key
+ * index j; a zero stride broadcasts that axis; `h` indexes QUERY heads.
+ * A query row whose every key is masked produces an all-zero output row. */
+typedef enum {
+    SDPA_MASK_NONE = 0,
+    SDPA_MASK_ADDITIVE = 1,
+    SDPA_MASK_BOOLEAN = 2,
+    SDPA_MASK_CAUSAL = 3
+} sdpa_mask_kind;
+
+/* Kernels (mlx issue #3885, "Current routing": vector for qL <= 8, full for qL > 8). */
+typedef enum {
+    SDPA_KERNEL_UNSUPPORTED = 0, /* this shape has no fused kernel: an error, never a fallback */
+    SDPA_KERNEL_FULL = 1,        /* prefill: q_len > 8, MFMA tiles, online softmax        */
+    SDPA_KERNEL_VECTOR = 2       /* decode: q_len <= 8, split keys + log-sum-exp combine  */
+} sdpa_kernel;
+
+typedef struct {
+    int64_t b, h, l, d;
+} sdpa_strides;
+
+/* Status codes. */
+#define SDPA_OK 0
+#define SDPA_EINVAL (-1)       /* null pointer, non-positive size, Hq % Hkv != 0, bad mask args */
+#define SDPA_EUNSUPPORTED (-2) /* head dim / dtype not built, d stride != 1, misaligned          */
+#define SDPA_EWORKSPACE (-3)   /* workspace smaller than sdpa_workspace_size()                   */
+#define SDPA_ELAUNCH (-4)      /* launch shape rejected by the kernel's own limits               */
+#define SDPA_EHIP (-5)         /* a HIP runtime call failed (detail: sdpa_last_hip_error())      */
+
+/* Reasons reported by sdpa_select_kernel (0 when a kernel is selected). */
+#define SDPA_REASON_OK 0
+#define SDPA_REASON_HEAD_DIM 1   /* head_dim is not one of the built sizes      */
+#define SDPA_REASON_DTYPE 2      /* dtype is not F32 / F16 / BF16              */
+#define SDPA_REASON_GROUPS 3     /* n_q_heads is not a multiple of n_kv_heads  */
+#define SDPA_REASON_SIZE 4       /* a size is non-positive or too large        */
+#define SDPA_REASON_MASK 5       /* unknown mask kind                          */
+
+/*
+ * sdpa_forward -- O = softmax(scale * Q K^T + M) V.
+ *
+ *   q, k, v, out   device pointers of element type `dtype`, with the logical
+ *                  strides q_st, k_st, v_st, o_st described above.  `out` may
+ *                  not overlap q, k, v or the workspace.
+ *   batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim   all >= 1.
+ *   scale          multiplies Q K^T (pass 1/sqrt(head_dim) for the usual scale).
+ *   mask_kind      see sdpa_mask_kind.  `mask`, `mask_st` and `mask_dtype` are
+ *                  read only for ADDITIVE (mask_dtype = dtype or SDPA_F32) and
+ *                  BOOLEAN (mask_dtype = SDPA_U8); mask must then be non-null.
+ *   workspace      device scratch of at least sdpa_workspace_size(...) bytes,
+ *                  256-byte aligned (may be NULL when that size is 0).  The
+ *                  vector kernel writes its per-split partial results there
+ *                  and reads them back within the same call; the contents
+ *                  need no initialisation and are garbage afterwards.  Calls
+ *                  that share a workspace must be ordered on one stream.
+ *   stream         hipStream_t as void*.
+ * Returns SDPA_OK or a negative status; nothing is enqueued on error.
+ */
+int sdpa_forward(const void* q, sdpa_strides q_st,
+                 const void* k, sdpa_strides k_st,
+                 const void* v, sdpa_strides v_st,
+                 void* out, sdpa_strides o_st,
+                 int batch, int q_len, int kv_len,
+                 int n_q_heads, int n_kv_heads, int head_dim,
+                 sdpa_dtype dtype, float scale,
+                 sdpa_mask_kind mask_kind, const void* mask, sdpa_strides mask_st,
+                 sdpa_dtype mask_dtype,
+                 void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * sdpa_select_kernel -- the predicate sdpa_forward itself uses (one shared
+ * function, so the query and the launch can never disagree; mlxcel issue
+ * #1065 shows an inline copy of such a test drifting from the shared one).
+ * Host only; touches no GPU.  Writes the kernel to *kernel and the reason
+ * (SDPA_REASON_*) to *reason (either pointer may be NULL).  Returns SDPA_OK
+ * when a kernel is selected, SDPA_EUNSUPPORTED or SDPA_EINVAL otherwise.
+ */
+int sdpa_select_kernel(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads,
+                       int head_dim, sdpa_dtype dtype, sdpa_mask_kind mask_kind,
+                       sdpa_kernel* kernel, int* reason);
+
+/*
+ * sdpa_describe_route -- human-readable route for the same arguments: kernel,
+ * tile shape, waves, key splits (e.g. "vector bf16 d512 additive splits=64").
+ * Host only.  Writes a NUL-terminated string of at most `len` bytes into buf.
+ * Returns the same status as sdpa_select_kernel.
+ */
+int sdpa_describe_route(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads,
+                        int head_dim, sdpa_dtype dtype, sdpa_mask_kind mask_kind,
+                        char* buf, size_t len);
+
+/*
+ * sdpa_workspace_size -- bytes of workspace sdpa_forward needs for this shape:
+ * 0 for the full kernel; for the vector kernel the per-split partial results
+ * (an fp32 output row plus running max and sum, per split, query head and
+ * query row).  Returns 0 for unsupported shapes as well.  The mask kind does
+ * not change the size.
+ */
+size_t sdpa_workspace_size(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads,
+                           int head_dim, sdpa_dtype dtype);
+
+/* sdpa_head_dims -- writes up to n built head dims (ascending) to out; returns how many exist. */
+int sdpa_head_dims(int* out, int n);
+
+/* sdpa_strerror -- static description of a status code (never NULL). */
+const char* sdpa_strerror(int status);
+
+/* sdpa_last_hip_error -- the hipError_t of the last SDPA_EHIP on this thread (0 if none). */
+int sdpa_last_hip_error(void);
+
+/*
+ * sdpa_route_counters -- diagnostics: copies up to n counters into out and
+ * returns how many exist: [0] calls, [1] full launches, [2] vector launches,
+ * [3] rejected (any error status).  calls == full + vector + rejected.
+ */
+int sdpa_route_counters(uint64_t* out, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_H */

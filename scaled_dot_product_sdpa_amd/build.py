@@ -1,0 +1,90 @@
+"""Build libsdpa.so for gfx950 with hipcc (in-tree, no JIT cache).
+
+    python -m scaled_dot_product_sdpa_amd.build [--jobs N]
+
+Every call recompiles.  The per-head-dim instantiation units are generated
+from csrc/inst_template.hip.in into _build/ and compiled in parallel.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import re
+import shutil
+import subprocess
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libsdpa.so")
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed-fp32 VALU forms are kept out of the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def head_dims() -> list[int]:
+    src = open(os.path.join(CSRC, "launch.h")).read()
+    m = re.search(r"#define SDPA_HEAD_DIMS\(X\)(.*)", src)
+    return [int(x) for x in re.findall(r"X\((\d+)\)", m.group(1))]
+
+
+def _run(cmd):
+    t = time.time()
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{err}")
+    return time.time() - t, err
+
+
+def build(jobs: int | None = None, verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    tmpl = open(os.path.join(CSRC, "inst_template.hip.in")).read()
+    units = []
+    for d in head_dims():
+        path = os.path.join(BUILD, f"inst_d{d}.hip")
+        text = tmpl.replace("@D@", str(d))
+        if not os.path.exists(path) or open(path).read() != text:
+            with open(path, "w") as f:
+                f.write(text)
+        units.append(path)
+    units.append(os.path.join(CSRC, "sdpa_host.cpp"))
+    objs = []
+    cmds = []
+    for u in units:
+        o = os.path.join(BUILD, os.path.basename(u) + ".o")
+        objs.append(o)
+        lang = ["-x", "hip"] if u.endswith(".cpp") else []
+        cmds.append([HIPCC] + COMMON + lang + ["-c", u, "-o", o])
+    jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        for cmd, (dt, err) in zip(cmds, ex.map(_run, cmds)):
+            if verbose:
+                print(f"[build] {os.path.basename(cmd[-3])}: {dt:.1f}s", flush=True)
+            if err.strip() and verbose:
+                print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"[build] {LIB} ({time.time() - t0:.1f}s)", flush=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=None)
+    a = ap.parse_args()
+    build(a.jobs)

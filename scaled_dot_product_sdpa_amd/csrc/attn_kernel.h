@@ -1,0 +1,447 @@
+// Fused attention tile kernel for gfx950 (MI355X), shared by the prefill
+// ("full") path and the split-key decode ("vector") path, plus the decode
+// combine kernel.
+//
+// What it computes: O = softmax(scale * Q K^T + M) V per (batch, query head),
+// key/value head = query head / n_rep (mlx issue #3885, prefill paragraph:
+// scores are [B, n_kv, n_rep, qL, kL]), masks none / additive / boolean /
+// causal (mlx PR #4330, "Proposed changes"), the softmax taken over the keys
+// (mlx issue #3585, "Reproduction").  Scores are never written to memory:
+// each key tile updates a running maximum m, running sum l and the output
+// accumulator, rescaled by 2^(m_old - m_new) (online softmax, base-2
+// exponent with log2(e) folded into the scale).
+//
+// Work decomposition (one workgroup):
+//   * WM x WD waves; a wave owns 32 query columns (MFMA N axis) and, when
+//     WD > 1, one D/WD slice of the head dimension.  With WD > 1 the waves of
+//     one column block each contract their slice of Q K^T and sum the
+//     partial scores through LDS in a fixed order (so every wave holds the
+//     same scores), then each accumulates its own slice of O: the O
+//     accumulator of a 512-wide head is spread over 4 waves instead of one.
+//   * K/V tiles of BN keys: global -> registers (prefetched one tile ahead)
+//     -> LDS.  K is stored row-major [key][d] (+16 B row pad against bank
+//     conflicts); V is stored transposed [d][key] so that each lane reads the
+//     four consecutive keys its P registers hold at a fixed d.
+//   * Head dims that are not a multiple of the MFMA K step (72 = 4.5 x 16)
+//     are zero-padded in LDS and in the Q fragments; when D % 32 != 0 the V^T
+//     tile has spare rows and row D is set to ones, so the MFMA produces the
+//     softmax row sums along with O (already rescaled with it).
+//   * Prefill grid: (query tiles, Hq, B); causal launches the longest tiles
+//     first and stops at the diagonal (bottom-right aligned).  Decode grid:
+//     (key splits, Hkv * column groups, B); a column enumerates
+//     (query head in the group, query row), so all n_rep query heads of a
+//     key/value head share every K/V byte read.
+#pragma once
+
+#include "attn_common.h"
+
+namespace sdpa_dev {
+
+template <class TR, int D_, int BN_, int WM_, int WD_>
+struct TileCfg {
+    static constexpr int D = D_, BN = BN_, WM = WM_, WD = WD_;
+    static constexpr int NW = WM * WD, NT = 64 * NW;
+    static constexpr int ES = TR::ES, EPC = TR::EPC, KCH = TR::KCH;
+    static constexpr int DW = D / WD;
+    static constexpr int NCH = (DW + KCH - 1) / KCH;           // score chunks per wave
+    static constexpr int DKP = (WD == 1) ? NCH * KCH : D;      // K tile columns incl. zero pad
+    static constexpr int KP = DKP + 16 / ES;                   // K row pitch (elements)
+    static constexpr int NDB = (DW + 31) / 32;                 // 32-row O^T blocks per wave
+    static constexpr int DVP = (WD == 1) ? NDB * 32 : D;       // V^T rows incl. pad
+    static constexpr int VP = BN + 16 / ES;                    // V^T row pitch (elements)
+    static constexpr int NKB = BN / 32;                        // 32-key score blocks per tile
+    static constexpr bool ONES = (D % 32) != 0;
+    static constexpr int KCPR = D / EPC;                       // 16-byte chunks per K/V row
+    static constexpr int UK = (BN * KCPR + NT - 1) / NT;       // K chunks per thread per tile
+    static constexpr int UV = ((BN / 4) * KCPR + NT - 1) / NT; // V 4-key units per thread per tile
+    static constexpr int LDS_K = BN * KP * ES;
+    static constexpr int LDS_V = DVP * VP * ES;
+    static constexpr int LDS_X = (WD > 1) ? WM * WD * 32 * BN * 4 : 0;
+    static constexpr int LDS = LDS_K + LDS_V + LDS_X;
+    static_assert(D % WD == 0, "head dim split");
+    static_assert(WD == 1 || (DW % 32 == 0 && DW % KCH == 0), "split-D slices must be whole blocks");
+    static_assert(D % EPC == 0, "head dim must be a whole number of 16-byte chunks");
+    static_assert(BN % 32 == 0, "key tile");
+    static_assert(!ONES || WD == 1, "row-sum row needs a spare V^T row");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <class TR> struct OneBits;
+template <> struct OneBits<TBF16> { static constexpr uint32_t v = 0x3F80u; };
+template <> struct OneBits<TF16> { static constexpr uint32_t v = 0x3C00u; };
+template <> struct OneBits<TF32> { static constexpr uint32_t v = 0x3F800000u; };
+
+template <class TR, class C, int MASK, bool DECODE>
+__global__ __launch_bounds__(C::NT) void attn_tile_kernel(const Params p) {
+    constexpr int ES = C::ES, EPC = C::EPC, KCH = C::KCH, BN = C::BN, D = C::D, DW = C::DW;
+    constexpr float NEG_INF = -__builtin_inff();
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    char* const Ks = smem;
+    char* const Vt = smem + C::LDS_K;
+    float* const X = reinterpret_cast<float*>(smem + C::LDS_K + C::LDS_V);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WD, wd = wave % C::WD;
+    const int col = lane & 31, hh = lane >> 5;
+    const int b = blockIdx.z;
+
+    // ---- columns -> (query head, query row); key range of this workgroup ----
+    int g, qh, qi, split = 0;
+    bool rv;
+    int kbeg, kend;
+    if constexpr (!DECODE) {
+        int t = blockIdx.x;
+        if (MASK == MASK_CAUSAL) t = (int)gridDim.x - 1 - t;  // longest causal tiles first
+        qh = blockIdx.y;
+        g = qh / p.n_rep;
+        const int i0 = t * 32 * C::WM;
+        qi = i0 + 32 * wm + col;
+        rv = qi < p.Lq;
+        kbeg = 0;
+        kend = p.Lk;
+        if (MASK == MASK_CAUSAL) {
+            const int64_t e = (int64_t)i0 + 32 * C::WM + (p.Lk - p.Lq);
+            kend = (int)(e < 0 ? 0 : (e > p.Lk ? p.Lk : e));
+        }
+    } else {
+        split = blockIdx.x;
+        g = blockIdx.y / p.col_groups;
+        const int cg = blockIdx.y % p.col_groups;
+        const int r = cg * 32 * C::WM + 32 * wm + col;
+        rv = r < p.n_rep * p.Lq;
+        const int rr = rv ? r : 0;
+        qh = g * p.n_rep + rr / p.Lq;
+        qi = rr % p.Lq;
+        kbeg = split * p.keys_per_split;
+        kend = min(p.Lk, kbeg + p.keys_per_split);
+    }
+    const int off = p.Lk - p.Lq;  // bottom-right causal alignment
+    const char* const kglob = reinterpret_cast<const char*>(p.k) +
+                              ((int64_t)b * p.ks[0] + (int64_t)g * p.ks[1]) * ES;
+    const char* const vglob = reinterpret_cast<const char*>(p.v) +
+                              ((int64_t)b * p.vs[0] + (int64_t)g * p.vs[1]) * ES;
+
+    // ---- Q fragments (MFMA B operand), zero beyond D / beyond the rows ----
+    u32x4_t qf[C::NCH];
+    {
+        const char* qrow = reinterpret_cast<const char*>(p.q) +
+                           ((int64_t)b * p.qs[0] + (int64_t)qh * p.qs[1] + (int64_t)qi * p.qs[2]) * ES;
+#pragma unroll
+        for (int ch = 0; ch < C::NCH; ++ch) {
+            const int d = wd * DW + ch * KCH + hh * EPC;
+            u32x4_t z = {0u, 0u, 0u, 0u};
+            qf[ch] = (rv && d < D) ? *reinterpret_cast<const u32x4_t*>(qrow + (int64_t)d * ES) : z;
+        }
+    }
+
+    // ---- constant LDS pads: K columns [D, DKP) = 0; V^T rows [D, DVP) = 0 (row D = 1) ----
+    if constexpr (C::DKP > D) {
+        constexpr int PADC = C::DKP - D;
+        for (int idx = tid; idx < BN * PADC; idx += C::NT) {
+            const int key = idx / PADC, c = D + idx % PADC;
+            if constexpr (ES == 2) reinterpret_cast<uint16_t*>(Ks)[key * C::KP + c] = 0;
+            else reinterpret_cast<uint32_t*>(Ks)[key * C::KP + c] = 0;
+        }
+    }
+    if constexpr (C::DVP > D) {
+        for (int idx = tid; idx < (C::DVP - D) * BN; idx += C::NT) {
+            const int row = D + idx / BN, j = idx % BN;
+            const uint32_t val = (C::ONES && row == D) ? OneBits<TR>::v : 0u;
+            if constexpr (ES == 2) reinterpret_cast<uint16_t*>(Vt)[row * C::VP + j] = (uint16_t)val;
+            else reinterpret_cast<uint32_t*>(Vt)[row * C::VP + j] = val;
+        }
+    }
+
+    // ---- tile loader: global -> registers, registers -> LDS ----
+    u32x4_t kr[C::UK];
+    u32x4_t vr[C::UV][4];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int u = 0; u < C::UK; ++u) {
+            const int idx = tid + u * C::NT;
+            kr[u] = u32x4_t{0u, 0u, 0u, 0u};
+            if (idx < BN * C::KCPR) {
+                const int key = idx / C::KCPR, c = idx % C::KCPR;
+                const int j = kt + key;
+                if (j < kend)
+                    kr[u] = *reinterpret_cast<const u32x4_t*>(kglob + ((int64_t)j * p.ks[2] + c * EPC) * ES);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < C::UV; ++u) {
+            const int idx = tid + u * C::NT;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vr[u][r] = u32x4_t{0u, 0u, 0u, 0u};
+            if (idx < (BN / 4) * C::KCPR) {
+                const int q4 = idx / C::KCPR, c = idx % C::KCPR;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = kt + 4 * q4 + r;
+                    if (j < kend)
+                        vr[u][r] = *reinterpret_cast<const u32x4_t*>(vglob + ((int64_t)j * p.vs[2] + c * EPC) * ES);
+                }
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int u = 0; u < C::UK; ++u) {
+            const int idx = tid + u * C::NT;
+            if (idx < BN * C::KCPR) {
+                const int key = idx / C::KCPR, c = idx % C::KCPR;
+                *reinterpret_cast<u32x4_t*>(Ks + (key * C::KP + c * EPC) * ES) = kr[u];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < C::UV; ++u) {
+            const int idx = tid + u * C::NT;
+            if (idx < (BN / 4) * C::KCPR) {
+                const int q4 = idx / C::KCPR, c = idx % C::KCPR;
+                if constexpr (ES == 2) {
+                    // 4 keys x 8 d -> 8 rows of V^T, 4 keys (8 bytes) each
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+                            const uint32_t lo = __builtin_amdgcn_perm(vr[u][1][w], vr[u][0][w], sel);
+                            const uint32_t hi = __builtin_amdgcn_perm(vr[u][3][w], vr[u][2][w], sel);
+                            const int d = c * 8 + 2 * w + e;
+                            *reinterpret_cast<u32x2_t*>(Vt + (d * C::VP + 4 * q4) * 2) = u32x2_t{lo, hi};
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int d = c * 4 + i;
+                        *reinterpret_cast<u32x4_t*>(Vt + (d * C::VP + 4 * q4) * 4) =
+                            u32x4_t{vr[u][0][i], vr[u][1][i], vr[u][2][i], vr[u][3][i]};
+                    }
+                }
+            }
+        }
+    };
+
+    // mask row of this lane's query (row 0 for padding columns: never used)
+    const int64_t mrow = (MASK == MASK_ADD || MASK == MASK_BOOL)
+                             ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)(rv ? qi : 0) * p.ms[2]
+                             : 0;
+
+    float m_run = NEG_INF, l_run = 0.f;
+    f32x16_t oacc[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16_t{};
+
+    if (kbeg < kend) load_tile(kbeg);
+    for (int kt = kbeg; kt < kend; kt += BN) {
+        __syncthreads();  // every wave is done reading the previous tile
+        store_tile();
+        __syncthreads();
+        if (kt + BN < kend) load_tile(kt + BN);  // next tile in flight during this one
+
+        // ---- S^T = K Q^T over this wave's slice of d ----
+        f32x16_t sacc[C::NKB];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+            sacc[kb] = f32x16_t{};
+#pragma unroll
+            for (int ch = 0; ch < C::NCH; ++ch) {
+                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+                    Ks + ((kb * 32 + col) * C::KP + wd * DW + ch * KCH + hh * EPC) * ES);
+                sacc[kb] = TR::mma(a, qf[ch], sacc[kb]);
+            }
+        }
+        if constexpr (C::WD > 1) {
+            float* const mine = X + (wm * C::WD + wd) * 32 * BN;
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mine[(kb * 16 + r) * 64 + lane] = sacc[kb][r];
+            __syncthreads();
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int w = 0; w < C::WD; ++w) s += X[(wm * C::WD + w) * 32 * BN + (kb * 16 + r) * 64 + lane];
+                    sacc[kb][r] = s;
+                }
+        }
+
+        // ---- mask, running max ----
+        float mloc = NEG_INF;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int key0 = kt + kb * 32 + 8 * a4 + 4 * hh;
+                f32x4_t madd = {0.f, 0.f, 0.f, 0.f};
+                uint32_t mbits = 0x01010101u;
+                if constexpr (MASK == MASK_ADD || MASK == MASK_BOOL) {
+                    if (p.mask_vec && key0 + 3 < p.Lk) {
+                        if constexpr (MASK == MASK_ADD) madd = load_mask4(p.mask, mrow + key0, p.mask_dtype);
+                        else mbits = *reinterpret_cast<const uint32_t*>(
+                                 reinterpret_cast<const uint8_t*>(p.mask) + mrow + key0);
+                    } else {
+                        mbits = 0;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = key0 + r;
+                            if (j < p.Lk) {
+                                const int64_t o = mrow + (int64_t)j * p.ms[3];
+                                if constexpr (MASK == MASK_ADD) madd[r] = load_mask_scalar(p.mask, o, p.mask_dtype);
+                                else mbits |= (reinterpret_cast<const uint8_t*>(p.mask)[o] ? 1u : 0u) << (8 * r);
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = key0 + r;
+                    float x = sacc[kb][4 * a4 + r] * p.scale_log2;
+                    if constexpr (MASK == MASK_ADD) x = __builtin_fmaf(madd[r], kLog2e, x);
+                    bool ok = j < kend;
+                    if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
+                    if constexpr (MASK == MASK_BOOL) ok = ok && ((mbits >> (8 * r)) & 0xffu) != 0u;
+                    x = ok ? x : NEG_INF;
+                    sacc[kb][4 * a4 + r] = x;
+                    mloc = fmaxf(mloc, x);
+                }
+            }
+        }
+        mloc = fmaxf(mloc, xor32(mloc));
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
+        const float muse = (m_new == NEG_INF) ? 0.f : m_new;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = fast_exp2(sacc[kb][r] - muse);
+                sacc[kb][r] = e;
+                lsum += e;
+            }
+        if constexpr (!C::ONES) l_run = l_run * alpha + lsum;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+        // ---- O^T += V^T P^T ----
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+            for (int pc = 0; pc < 32 / KCH; ++pc) {
+                u32x4_t bf;
+                if constexpr (ES == 2) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        bf[w] = TR::pack(sacc[kb][8 * pc + 2 * w], sacc[kb][8 * pc + 2 * w + 1]);
+                } else {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) bf[w] = __float_as_uint(sacc[kb][4 * pc + w]);
+                }
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db) {
+                    const int d = wd * DW + 32 * db + col;
+                    u32x4_t af;
+                    if constexpr (ES == 2) {
+                        const u32x2_t x0 = *reinterpret_cast<const u32x2_t*>(
+                            Vt + (d * C::VP + kb * 32 + 16 * pc + 4 * hh) * 2);
+                        const u32x2_t x1 = *reinterpret_cast<const u32x2_t*>(
+                            Vt + (d * C::VP + kb * 32 + 16 * pc + 8 + 4 * hh) * 2);
+                        af = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
+                    } else {
+                        af = *reinterpret_cast<const u32x4_t*>(Vt + (d * C::VP + kb * 32 + 8 * pc + 4 * hh) * 4);
+                    }
+                    oacc[db] = TR::mma(af, bf, oacc[db]);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue ----
+    float lsum_row;
+    if constexpr (C::ONES) {
+        constexpr int rr = D % 32;
+        constexpr int RL = 4 * (rr / 8) + (rr % 4), HL = (rr % 8) / 4, DBL = D / 32;
+        const float x = oacc[DBL][RL];
+        const float y = xor32(x);
+        lsum_row = (hh == HL) ? x : y;
+    } else {
+        lsum_row = l_run + xor32(l_run);
+    }
+    if constexpr (!DECODE) {
+        if (rv) {
+            const float inv = lsum_row > 0.f ? 1.f / lsum_row : 0.f;
+            char* orow = reinterpret_cast<char*>(p.o) +
+                         ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2]) * ES;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int d0 = wd * DW + 32 * db + 8 * a4 + 4 * hh;
+                    if (d0 < D) {
+                        f32x4_t x = {oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv,
+                                     oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv};
+                        TR::store4(orow + (int64_t)d0 * ES, x);
+                    }
+                }
+        }
+    } else {
+        if (rv) {
+            const int64_t row = ((int64_t)b * p.Hq + qh) * p.Lq + qi;
+            float* po = p.ws_o + (row * p.splits + split) * D;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int d0 = wd * DW + 32 * db + 8 * a4 + 4 * hh;
+                    if (d0 < D)
+                        *reinterpret_cast<f32x4_t*>(po + d0) =
+                            f32x4_t{oacc[db][4 * a4], oacc[db][4 * a4 + 1], oacc[db][4 * a4 + 2], oacc[db][4 * a4 + 3]};
+                }
+            if (wd == 0 && hh == 0) {
+                p.ws_ml[(row * p.splits + split) * 2 + 0] = m_run;
+                p.ws_ml[(row * p.splits + split) * 2 + 1] = lsum_row;
+            }
+        }
+    }
+}
+
+// Decode combine: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, splits in
+// ascending order (deterministic).  grid = (B*Hq*Lq, ceil(D/256)), 256 threads.
+template <class TR, int D>
+__global__ __launch_bounds__(256) void combine_kernel(const Params p) {
+    constexpr int ES = TR::ES;
+    constexpr float NEG_INF = -__builtin_inff();
+    const int64_t row = blockIdx.x;
+    const int d = blockIdx.y * 256 + threadIdx.x;
+    const int S = p.splits;
+    const float* ml = p.ws_ml + row * S * 2;
+    float M = NEG_INF;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+    if (d >= D) return;
+    float num = 0.f, den = 0.f;
+    if (M != NEG_INF) {
+        const float* po = p.ws_o + row * S * D + d;
+        for (int s = 0; s < S; ++s) {
+            const float ms = ml[2 * s];
+            const float w = (ms == NEG_INF) ? 0.f : fast_exp2(ms - M);
+            num = __builtin_fmaf(w, po[(int64_t)s * D], num);
+            den = __builtin_fmaf(w, ml[2 * s + 1], den);
+        }
+    }
+    const float val = den > 0.f ? num / den : 0.f;
+    const int qi = (int)(row % p.Lq);
+    const int64_t bh = row / p.Lq;
+    const int qh = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+    char* dst = reinterpret_cast<char*>(p.o) +
+                ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2] + d) * ES;
+    TR::store1(dst, val);
+}
+
+}  // namespace sdpa_dev

@@ -1,0 +1,51 @@
+// Internal host-side launch table: one KernelSet per (element type, head dim).
+// Not part of the public ABI (see include/sdpa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "attn_common.h"
+
+namespace sdpa_host {
+
+using sdpa_dev::Params;
+
+typedef hipError_t (*launch_fn)(const Params&, dim3 grid, hipStream_t stream);
+
+struct TileInfo {
+    int bn;   // keys per tile
+    int wm;   // 32-column blocks per workgroup
+    int wd;   // waves splitting the head dim
+    int nt;   // threads per workgroup
+    int lds;  // bytes of LDS per workgroup
+};
+
+struct KernelSet {
+    launch_fn full[4];    // indexed by mask kind
+    launch_fn decode[4];  // indexed by mask kind
+    launch_fn combine;
+    TileInfo full_cfg;
+    TileInfo dec_cfg;
+};
+
+// Returns hipErrorInvalidConfiguration when the compiled kernel cannot run
+// `nt` threads per workgroup (register or LDS limits): such a launch would be
+// dropped by the hardware, so it is refused before it is made.
+template <class K>
+hipError_t check_launch_once(K kernel, int nt, hipError_t* cache, bool* done) {
+    if (*done) return *cache;
+    hipFuncAttributes a;
+    hipError_t e = hipFuncGetAttributes(&a, reinterpret_cast<const void*>(kernel));
+    if (e == hipSuccess && a.maxThreadsPerBlock < nt) e = hipErrorInvalidConfiguration;
+    *cache = e;
+    *done = true;
+    return e;
+}
+
+// Head dims with built kernels; one getter per head dim (index = sdpa_dtype: F32, F16, BF16).
+#define SDPA_HEAD_DIMS(X) X(64) X(72) X(80) X(96) X(128) X(256) X(512)
+#define SDPA_DECLARE_GETTER(D) const KernelSet* kernels_d##D(int dtype);
+SDPA_HEAD_DIMS(SDPA_DECLARE_GETTER)
+#undef SDPA_DECLARE_GETTER
+
+}  // namespace sdpa_host

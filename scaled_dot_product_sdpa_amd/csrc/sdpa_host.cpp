@@ -1,0 +1,400 @@
+// Host side of libsdpa.so: argument checks, the routing predicate, workspace
+// sizing, launches, diagnostics.  Implements include/sdpa.h.
+//
+// Routing follows mlx issue #3885 ("Current routing"): query length <= 8 ->
+// vector (decode) kernel, longer -> full (prefill) kernel.  Unlike the
+// routing that page describes, there is no unfused fallback: a head dim or
+// element type without a built kernel is reported as unsupported by the same
+// predicate the caller can query, and sdpa_forward returns an error for it.
+#include "../../include/sdpa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <set>
+#include <string>
+
+#include "launch.h"
+
+using sdpa_dev::Params;
+using sdpa_host::KernelSet;
+
+namespace {
+
+constexpr int kVectorMaxQLen = 8;     // qL <= 8 -> vector kernel
+constexpr int kDeviceCUs = 256;       // MI355X compute units (split heuristic only)
+constexpr int kMaxGridYZ = 65535;
+
+std::atomic<uint64_t> g_counters[4];  // calls, full, vector, rejected
+thread_local int g_last_hip_error = 0;
+
+const int kHeadDims[] = {
+#define SDPA_LIST_D(D) D,
+    SDPA_HEAD_DIMS(SDPA_LIST_D)
+#undef SDPA_LIST_D
+};
+
+const KernelSet* kernel_set(sdpa_dtype dt, int d) {
+    if (dt != SDPA_F32 && dt != SDPA_F16 && dt != SDPA_BF16) return nullptr;
+    switch (d) {
+#define SDPA_CASE_D(D) \
+    case D:            \
+        return sdpa_host::kernels_d##D((int)dt);
+        SDPA_HEAD_DIMS(SDPA_CASE_D)
+#undef SDPA_CASE_D
+        default:
+            return nullptr;
+    }
+}
+
+bool head_dim_built(int d) {
+    for (int x : kHeadDims)
+        if (x == d) return true;
+    return false;
+}
+
+int elem_size(sdpa_dtype dt) {
+    switch (dt) {
+        case SDPA_F32: return 4;
+        case SDPA_F16: return 2;
+        case SDPA_BF16: return 2;
+        case SDPA_U8: return 1;
+    }
+    return 0;
+}
+
+// The one routing predicate (also behind sdpa_select_kernel).
+int select(int batch, int q_len, int kv_len, int hq, int hkv, int d, sdpa_dtype dt, sdpa_mask_kind mk,
+           sdpa_kernel* kernel, int* reason) {
+    sdpa_kernel k = SDPA_KERNEL_UNSUPPORTED;
+    int why = SDPA_REASON_OK, st = SDPA_OK;
+    if (batch <= 0 || q_len <= 0 || kv_len <= 0 || hq <= 0 || hkv <= 0 || d <= 0 || batch > kMaxGridYZ ||
+        hq > kMaxGridYZ) {
+        why = SDPA_REASON_SIZE;
+        st = SDPA_EINVAL;
+    } else if (hq % hkv != 0) {
+        why = SDPA_REASON_GROUPS;
+        st = SDPA_EINVAL;
+    } else if (mk < SDPA_MASK_NONE || mk > SDPA_MASK_CAUSAL) {
+        why = SDPA_REASON_MASK;
+        st = SDPA_EINVAL;
+    } else if (dt != SDPA_F32 && dt != SDPA_F16 && dt != SDPA_BF16) {
+        why = SDPA_REASON_DTYPE;
+        st = SDPA_EUNSUPPORTED;
+    } else if (!head_dim_built(d)) {
+        why = SDPA_REASON_HEAD_DIM;
+        st = SDPA_EUNSUPPORTED;
+    } else {
+        k = (q_len <= kVectorMaxQLen) ? SDPA_KERNEL_VECTOR : SDPA_KERNEL_FULL;
+    }
+    if (kernel) *kernel = k;
+    if (reason) *reason = why;
+    return st;
+}
+
+struct DecodePlan {
+    int col_groups;
+    int splits;
+    int keys_per_split;
+};
+
+// Split the key axis so the decode grid covers the chip about twice; a
+// test-only environment override (SDPA_DECODE_SPLITS) pins the count.
+DecodePlan decode_plan(int batch, int q_len, int kv_len, int hq, int hkv, const sdpa_host::TileInfo& t) {
+    DecodePlan p;
+    const int rows = (hq / hkv) * q_len;
+    const int cols = 32 * t.wm;
+    p.col_groups = (rows + cols - 1) / cols;
+    const long groups = (long)batch * hkv * p.col_groups;
+    const int max_splits = (kv_len + t.bn - 1) / t.bn;
+    long s = (2L * kDeviceCUs + groups - 1) / groups;
+    if (const char* env = std::getenv("SDPA_DECODE_SPLITS")) {
+        const long v = std::strtol(env, nullptr, 10);
+        if (v > 0) s = v;
+    }
+    if (s < 1) s = 1;
+    if (s > max_splits) s = max_splits;
+    const int per = (int)((kv_len + s - 1) / s);
+    p.keys_per_split = ((per + t.bn - 1) / t.bn) * t.bn;
+    p.splits = (kv_len + p.keys_per_split - 1) / p.keys_per_split;
+    return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t decode_ws_bytes(int batch, int q_len, int hq, int d, const DecodePlan& p) {
+    const size_t rows = (size_t)batch * hq * q_len;
+    return align256(rows * p.splits * d * sizeof(float)) + align256(rows * p.splits * 2 * sizeof(float));
+}
+
+// Byte extent of a strided tensor: [base, base + span).
+size_t span_bytes(const int64_t* n, const sdpa_strides& s, int es) {
+    const int64_t st[4] = {s.b, s.h, s.l, s.d};
+    int64_t last = 0;
+    for (int i = 0; i < 4; ++i) last += (n[i] - 1) * st[i];
+    return (size_t)(last + 1) * es;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Strides must be non-negative, d stride 1, and every non-trivial axis a whole
+// number of 16-byte chunks (the kernels move Q, K, V, O in 16-byte vectors).
+int check_operand(const void* ptr, const sdpa_strides& s, const int64_t* n, int es) {
+    if (!ptr) return SDPA_EINVAL;
+    if (s.b < 0 || s.h < 0 || s.l < 0 || s.d < 0) return SDPA_EINVAL;
+    if (s.d != 1) return SDPA_EUNSUPPORTED;
+    if (((uintptr_t)ptr) % 16 != 0) return SDPA_EUNSUPPORTED;
+    const int64_t st[3] = {s.b, s.h, s.l};
+    for (int i = 0; i < 3; ++i)
+        if (n[i] > 1 && (st[i] * es) % 16 != 0) return SDPA_EUNSUPPORTED;
+    return SDPA_OK;
+}
+
+const char* dtype_name(sdpa_dtype dt) {
+    switch (dt) {
+        case SDPA_F32: return "f32";
+        case SDPA_F16: return "f16";
+        case SDPA_BF16: return "bf16";
+        case SDPA_U8: return "u8";
+    }
+    return "?";
+}
+
+const char* mask_name(sdpa_mask_kind mk) {
+    switch (mk) {
+        case SDPA_MASK_NONE: return "none";
+        case SDPA_MASK_ADDITIVE: return "additive";
+        case SDPA_MASK_BOOLEAN: return "boolean";
+        case SDPA_MASK_CAUSAL: return "causal";
+    }
+    return "?";
+}
+
+std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int d, sdpa_dtype dt,
+                         sdpa_mask_kind mk, int st, sdpa_kernel k, int reason) {
+    char buf[256];
+    if (st != SDPA_OK) {
+        std::snprintf(buf, sizeof buf, "unsupported (%s) B=%d Lq=%d Lk=%d Hq=%d Hkv=%d D=%d %s %s: reason %d",
+                      sdpa_strerror(st), batch, q_len, kv_len, hq, hkv, d, dtype_name(dt), mask_name(mk), reason);
+        return buf;
+    }
+    const KernelSet* ks = kernel_set(dt, d);
+    if (k == SDPA_KERNEL_FULL) {
+        const auto& t = ks->full_cfg;
+        std::snprintf(buf, sizeof buf,
+                      "full %s d%d %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d tile=%dx%d waves=%dx%d lds=%d",
+                      dtype_name(dt), d, mask_name(mk), batch, q_len, kv_len, hq, hkv, 32 * t.wm, t.bn, t.wm, t.wd,
+                      t.lds);
+    } else {
+        const auto& t = ks->dec_cfg;
+        DecodePlan p = decode_plan(batch, q_len, kv_len, hq, hkv, t);
+        std::snprintf(buf, sizeof buf,
+                      "vector %s d%d %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d splits=%d keys/split=%d colgroups=%d "
+                      "waves=%dx%d lds=%d",
+                      dtype_name(dt), d, mask_name(mk), batch, q_len, kv_len, hq, hkv, p.splits, p.keys_per_split,
+                      p.col_groups, t.wm, t.wd, t.lds);
+    }
+    return buf;
+}
+
+void log_route_once(const std::string& s) {
+    static const bool on = [] {
+        const char* e = std::getenv("SDPA_LOG_ROUTE");
+        return e && e[0] && e[0] != '0';
+    }();
+    if (!on) return;
+    static std::mutex mu;
+    static std::set<std::string> seen;
+    std::lock_guard<std::mutex> lock(mu);
+    if (seen.insert(s).second) std::fprintf(stderr, "[sdpa] %s\n", s.c_str());
+}
+
+int reject(int st) {
+    g_counters[3].fetch_add(1, std::memory_order_relaxed);
+    return st;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return SDPA_OK;
+    g_last_hip_error = (int)e;
+    if (e == hipErrorInvalidConfiguration) return SDPA_ELAUNCH;
+    return SDPA_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_select_kernel(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
+                       sdpa_dtype dtype, sdpa_mask_kind mask_kind, sdpa_kernel* kernel, int* reason) {
+    return select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, kernel, reason);
+}
+
+int sdpa_describe_route(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
+                        sdpa_dtype dtype, sdpa_mask_kind mask_kind, char* buf, size_t len) {
+    sdpa_kernel k;
+    int reason;
+    const int st = select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, &k, &reason);
+    if (buf && len) {
+        const std::string s =
+            route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, st, k, reason);
+        std::snprintf(buf, len, "%s", s.c_str());
+    }
+    return st;
+}
+
+size_t sdpa_workspace_size(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
+                           sdpa_dtype dtype) {
+    sdpa_kernel k;
+    if (select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, SDPA_MASK_NONE, &k, nullptr) !=
+            SDPA_OK ||
+        k != SDPA_KERNEL_VECTOR)
+        return 0;
+    const KernelSet* ks = kernel_set(dtype, head_dim);
+    const DecodePlan p = decode_plan(batch, q_len, kv_len, n_q_heads, n_kv_heads, ks->dec_cfg);
+    return decode_ws_bytes(batch, q_len, n_q_heads, head_dim, p);
+}
+
+int sdpa_head_dims(int* out, int n) {
+    const int total = (int)(sizeof(kHeadDims) / sizeof(kHeadDims[0]));
+    for (int i = 0; out && i < n && i < total; ++i) out[i] = kHeadDims[i];
+    return total;
+}
+
+const char* sdpa_strerror(int status) {
+    switch (status) {
+        case SDPA_OK: return "ok";
+        case SDPA_EINVAL: return "invalid argument";
+        case SDPA_EUNSUPPORTED: return "unsupported shape, type or layout (no fused kernel; no fallback)";
+        case SDPA_EWORKSPACE: return "workspace too small";
+        case SDPA_ELAUNCH: return "launch shape exceeds the kernel's limits";
+        case SDPA_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int sdpa_last_hip_error(void) { return g_last_hip_error; }
+
+int sdpa_route_counters(uint64_t* out, int n) {
+    for (int i = 0; out && i < n && i < 4; ++i) out[i] = g_counters[i].load(std::memory_order_relaxed);
+    return 4;
+}
+
+int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
+                 sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len, int n_q_heads,
+                 int n_kv_heads, int head_dim, sdpa_dtype dtype, float scale, sdpa_mask_kind mask_kind,
+                 const void* mask, sdpa_strides mask_st, sdpa_dtype mask_dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    g_counters[0].fetch_add(1, std::memory_order_relaxed);
+    sdpa_kernel kern;
+    int reason;
+    int st = select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, &kern, &reason);
+    if (st != SDPA_OK) return reject(st);
+    if (!std::isfinite(scale)) return reject(SDPA_EINVAL);
+
+    const int es = elem_size(dtype);
+    const int64_t nq[4] = {batch, n_q_heads, q_len, head_dim};
+    const int64_t nk[4] = {batch, n_kv_heads, kv_len, head_dim};
+    if ((st = check_operand(q, q_st, nq, es)) != SDPA_OK) return reject(st);
+    if ((st = check_operand(k, k_st, nk, es)) != SDPA_OK) return reject(st);
+    if ((st = check_operand(v, v_st, nk, es)) != SDPA_OK) return reject(st);
+    if ((st = check_operand(out, o_st, nq, es)) != SDPA_OK) return reject(st);
+    const size_t oq = span_bytes(nq, o_st, es);
+    if (overlaps(out, oq, q, span_bytes(nq, q_st, es)) || overlaps(out, oq, k, span_bytes(nk, k_st, es)) ||
+        overlaps(out, oq, v, span_bytes(nk, v_st, es)))
+        return reject(SDPA_EINVAL);
+
+    Params p{};
+    int mvec = 0;
+    if (mask_kind == SDPA_MASK_ADDITIVE || mask_kind == SDPA_MASK_BOOLEAN) {
+        if (!mask) return reject(SDPA_EINVAL);
+        if (mask_kind == SDPA_MASK_BOOLEAN && mask_dtype != SDPA_U8) return reject(SDPA_EINVAL);
+        if (mask_kind == SDPA_MASK_ADDITIVE && mask_dtype != SDPA_F32 && mask_dtype != SDPA_F16 &&
+            mask_dtype != SDPA_BF16)
+            return reject(SDPA_EINVAL);
+        if (mask_st.b < 0 || mask_st.h < 0 || mask_st.l < 0 || mask_st.d < 0) return reject(SDPA_EINVAL);
+        const int mes = elem_size(mask_dtype);
+        if (((uintptr_t)mask) % mes != 0) return reject(SDPA_EUNSUPPORTED);
+        // Vector mask loads need 4-key runs aligned to 4 elements.
+        mvec = mask_st.d == 1 && ((uintptr_t)mask) % (4 * mes) == 0 && mask_st.b % 4 == 0 && mask_st.h % 4 == 0 &&
+               mask_st.l % 4 == 0;
+        p.mask = mask;
+        p.ms[0] = mask_st.b;
+        p.ms[1] = mask_st.h;
+        p.ms[2] = mask_st.l;
+        p.ms[3] = mask_st.d;
+        p.mask_dtype = (int)mask_dtype;
+    }
+    p.mask_vec = mvec;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = out;
+    const sdpa_strides* sts[4] = {&q_st, &k_st, &v_st, &o_st};
+    int64_t* dst[4] = {p.qs, p.ks, p.vs, p.os};
+    for (int i = 0; i < 4; ++i) {
+        dst[i][0] = sts[i]->b;
+        dst[i][1] = sts[i]->h;
+        dst[i][2] = sts[i]->l;
+        dst[i][3] = sts[i]->d;
+    }
+    p.B = batch;
+    p.Lq = q_len;
+    p.Lk = kv_len;
+    p.Hq = n_q_heads;
+    p.Hkv = n_kv_heads;
+    p.n_rep = n_q_heads / n_kv_heads;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+
+    const KernelSet* ks = kernel_set(dtype, head_dim);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int mk = (int)mask_kind;
+
+    if (kern == SDPA_KERNEL_FULL) {
+        const auto& t = ks->full_cfg;
+        const int bm = 32 * t.wm;
+        dim3 grid((unsigned)((q_len + bm - 1) / bm), (unsigned)n_q_heads, (unsigned)batch);
+        log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, st,
+                                    kern, reason));
+        st = hip_status(ks->full[mk](p, grid, s));
+        if (st != SDPA_OK) return reject(st);
+        g_counters[1].fetch_add(1, std::memory_order_relaxed);
+        return SDPA_OK;
+    }
+
+    // vector (decode): split keys, then combine the splits
+    const auto& t = ks->dec_cfg;
+    const DecodePlan plan = decode_plan(batch, q_len, kv_len, n_q_heads, n_kv_heads, t);
+    const size_t need = decode_ws_bytes(batch, q_len, n_q_heads, head_dim, plan);
+    if (!workspace || workspace_bytes < need) return reject(SDPA_EWORKSPACE);
+    if (((uintptr_t)workspace) % 256 != 0) return reject(SDPA_EINVAL);
+    if (overlaps(out, oq, workspace, need)) return reject(SDPA_EINVAL);
+    if ((long)n_kv_heads * plan.col_groups > kMaxGridYZ) return reject(SDPA_EUNSUPPORTED);
+    const size_t rows = (size_t)batch * n_q_heads * q_len;
+    p.ws_o = reinterpret_cast<float*>(workspace);
+    p.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                       align256(rows * plan.splits * head_dim * sizeof(float)));
+    p.splits = plan.splits;
+    p.keys_per_split = plan.keys_per_split;
+    p.col_groups = plan.col_groups;
+    log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, st, kern,
+                                reason));
+    dim3 grid((unsigned)plan.splits, (unsigned)(n_kv_heads * plan.col_groups), (unsigned)batch);
+    st = hip_status(ks->decode[mk](p, grid, s));
+    if (st != SDPA_OK) return reject(st);
+    dim3 cgrid((unsigned)rows, (unsigned)((head_dim + 255) / 256), 1);
+    st = hip_status(ks->combine(p, cgrid, s));
+    if (st != SDPA_OK) return reject(st);
+    g_counters[2].fetch_add(1, std::memory_order_relaxed);
+    return SDPA_OK;
+}
+
+}  // extern "C"

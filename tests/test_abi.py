@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: exported symbols, the routing predicate,
+workspace sizing, status strings and argument validation (every case here is
+rejected before the library touches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import scaled_dot_product_sdpa_amd as sdpa
+from scaled_dot_product_sdpa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdpa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sdpa.LIB_PATH):
+        pytest.fail("libsdpa.so is not built (run __graft_entry__.build())")
+    return sdpa.load()
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(sdpa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_header_symbol(lib):
+    names = _header_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_head_dims(lib):
+    assert sdpa.head_dims() == [64, 72, 80, 96, 128, 256, 512]
+
+
+@pytest.mark.parametrize("q_len,kernel", [(1, "vector"), (8, "vector"), (9, "full"), (8192, "full")])
+def test_route_by_query_length(lib, q_len, kernel):
+    k, r, st = sdpa.select_kernel(1, q_len, 4096, 32, 4, 512, 2)
+    assert (k, r, st) == (kernel, 0, 0)
+
+
+@pytest.mark.parametrize("args,reason,status", [
+    ((1, 9, 9, 8, 3, 64, 2), 3, -1),        # Hq % Hkv != 0
+    ((1, 9, 9, 8, 4, 65, 2), 1, -2),        # head dim not built
+    ((1, 9, 9, 8, 4, 192, 0), 1, -2),
+    ((1, 9, 9, 8, 4, 64, 3), 2, -2),        # u8 is a mask type only
+    ((0, 9, 9, 8, 4, 64, 2), 4, -1),        # empty batch
+    ((1, 0, 9, 8, 4, 64, 2), 4, -1),
+    ((1, 9, 0, 8, 4, 64, 2), 4, -1),
+])
+def test_unsupported_is_an_error_with_a_reason(lib, args, reason, status):
+    k, r, st = sdpa.select_kernel(*args)
+    assert (k, r, st) == ("unsupported", reason, status)
+
+
+def test_every_dtype_and_head_dim_is_fused(lib):
+    for d in sdpa.head_dims():
+        for dt in (0, 1, 2):
+            for mk in ("none", "additive", "boolean", "causal"):
+                assert sdpa.select_kernel(2, 100, 100, 8, 2, d, dt, mk)[0] == "full"
+                assert sdpa.select_kernel(2, 1, 100, 8, 2, d, dt, mk)[0] == "vector"
+
+
+def test_describe_route(lib):
+    s = sdpa.describe_route(1, 1, 4096, 32, 4, 512, 2, "additive")
+    assert s.startswith("vector bf16 d512 additive") and "splits=" in s
+    s = sdpa.describe_route(1, 8192, 8192, 16, 16, 72, 2, "causal")
+    assert s.startswith("full bf16 d72 causal")
+    assert sdpa.describe_route(1, 9, 9, 8, 4, 65, 2).startswith("unsupported")
+
+
+def test_workspace_size(lib):
+    assert sdpa.workspace_size(1, 100, 100, 8, 2, 64, 2) == 0          # full kernel needs none
+    ws = sdpa.workspace_size(1, 1, 4096, 32, 4, 512, 2)
+    m = re.search(r"splits=(\d+)", sdpa.describe_route(1, 1, 4096, 32, 4, 512, 2))
+    s = int(m.group(1))
+    rows = 32
+    align = lambda x: (x + 255) // 256 * 256
+    assert ws == align(rows * s * 512 * 4) + align(rows * s * 2 * 4)
+    assert sdpa.workspace_size(1, 1, 4096, 32, 4, 65, 2) == 0
+
+
+def test_split_override_changes_the_plan(lib, monkeypatch):
+    monkeypatch.setenv("SDPA_DECODE_SPLITS", "3")
+    assert "splits=3 " in sdpa.describe_route(1, 1, 4096, 32, 8, 256, 2)
+
+
+def test_strerror_covers_every_status(lib):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.sdpa_strerror(st)
+    assert lib.sdpa_strerror(-99) == b"unknown status"
+
+
+def _forward(lib, q=16, k=16, v=16, o=4096, st=None, dims=(1, 16, 16, 2, 2, 64), dt=2, mk=0, mask=None,
+             mdt=3, ws=None, wsb=0):
+    S = _lib.Strides
+    st = st or S(2 * 16 * 64, 16 * 64, 64, 1)
+    return lib.sdpa_forward(q, st, k, st, v, st, o, st, *dims, dt, 0.125, mk, mask, S(0, 0, 0, 1), mdt,
+                            ws, wsb, None)
+
+
+def test_forward_rejects_bad_arguments_before_touching_the_gpu(lib):
+    before = sdpa.route_counters()
+    S = _lib.Strides
+    assert _forward(lib, q=None) == -1                                 # null pointer
+    assert _forward(lib, dims=(1, 16, 16, 3, 2, 64)) == -1             # groups
+    assert _forward(lib, dims=(1, 16, 16, 2, 2, 48)) == -2             # head dim
+    assert _forward(lib, st=S(2048, 1024, 64, 2)) == -2                # d stride != 1
+    assert _forward(lib, st=S(2048, 1024, 60, 1)) == -2                # row stride not 16-byte aligned
+    assert _forward(lib, q=24) == -2                                   # misaligned base
+    assert _forward(lib, st=S(-2048, 1024, 64, 1)) == -1               # negative stride
+    assert _forward(lib, o=16) == -1                                   # out overlaps q
+    assert _forward(lib, mk=1, mask=None) == -1                        # additive without mask
+    assert _forward(lib, mk=2, mask=4096 * 64, mdt=2) == -1            # boolean mask must be u8
+    assert _forward(lib, mk=1, mask=4096 * 64, mdt=3) == -1            # additive mask can't be u8
+    assert _forward(lib, mk=7) == -1                                   # unknown mask kind
+    assert _forward(lib, o=1 << 20, dims=(1, 1, 16, 2, 2, 64), ws=None, wsb=0) == -3  # decode workspace
+    after = sdpa.route_counters()
+    assert after["calls"] - before["calls"] == 13
+    assert after["rejected"] - before["rejected"] == 13
+    assert after["calls"] == after["full"] + after["vector"] + after["rejected"]

@@ -1,0 +1,142 @@
+"""GPU invariants: bitwise identities, determinism, split consistency, masks, memory."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import sdpa_inputs as si
+from gpu_util import assert_parity, oracle_out, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("D,dtype", [(72, "bf16"), (128, "f16"), (512, "bf16"), (64, "f32")])
+def test_causal_row0_is_v0_bitwise(gpu_lib, D, dtype):
+    c = si.make_case(1, 4, 2, 100, 100, D, dtype=dtype, mask_kind="causal", seed=3)
+    out = run_gpu(c).cpu()
+    v0 = c.v[:, :, :1].repeat_interleave(2, dim=1)
+    assert torch.equal(out[:, :, 0:1], v0)
+
+
+@pytest.mark.parametrize("lq", [1, 200])
+def test_layout_permutation_is_bitwise_identical(gpu_lib, lq):
+    a = si.make_case(1, 8, 4, lq, 300, 72, dtype="bf16", layout="blhd", mask_kind="causal", seed=11)
+    b = si.Case(a.q.contiguous(), a.k.contiguous(), a.v.contiguous(), a.scale, "causal", None, "bhld")
+    assert torch.equal(run_gpu(a), run_gpu(b))
+
+
+@pytest.mark.parametrize("lq", [1, 150])
+def test_run_to_run_determinism(gpu_lib, lq):
+    c = si.make_case(1, 8, 2, lq, 3000, 256, dtype="bf16", mask_kind="additive", seed=5)
+    outs = [run_gpu(c) for _ in range(3)]
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_forced_split_counts_agree(gpu_lib, monkeypatch):
+    c = si.make_case(1, 8, 2, 2, 1000, 128, dtype="f32", mask_kind="additive", seed=9)
+    ref = oracle_out(c)
+    outs = []
+    for s in ("1", "3", "7", "16"):
+        monkeypatch.setenv("SDPA_DECODE_SPLITS", s)
+        out = run_gpu(c)
+        assert_parity(out, ref, "f32", f"splits={s}")
+        outs.append(out)
+    for o in outs[1:]:
+        assert (o - outs[0]).abs().max().item() <= 2e-6
+
+
+def test_decode_matches_last_row_of_prefill(gpu_lib):
+    """q_len = 1 (vector kernel) vs the last row of a causal q_len = 64 call (full kernel)."""
+    full = si.make_case(1, 8, 2, 64, 300, 128, dtype="bf16", mask_kind="causal", seed=21)
+    one = si.Case(full.q[:, :, -1:], full.k, full.v, full.scale, "causal")
+    a = run_gpu(full)[:, :, -1:].float()
+    b = run_gpu(one).float()
+    assert (a - b).abs().max().item() <= 1e-2
+
+
+def test_query_chunks_match_the_block_call(gpu_lib):
+    """Chunked queries (bottom-right causal against the keys so far) = one block call."""
+    c = si.make_case(1, 4, 4, 96, 96, 64, dtype="f32", mask_kind="causal", seed=4)
+    whole = run_gpu(c)
+    for s, e in ((0, 1), (1, 9), (9, 40), (40, 96)):
+        part = si.Case(c.q[:, :, s:e], c.k[:, :, :e], c.v[:, :, :e], c.scale, "causal")
+        got = run_gpu(part)
+        assert (got - whole[:, :, s:e]).abs().max().item() <= 2e-6, (s, e)
+
+
+def test_boolean_equals_additive_minus_inf_bitwise(gpu_lib):
+    c = si.make_case(1, 4, 2, 70, 200, 80, dtype="bf16", mask_kind="boolean", seed=8, mask_shape="qk", mask_p=0.3)
+    add = torch.where(c.mask.bool(), torch.tensor(0.0), torch.tensor(-float("inf"))).to(torch.bfloat16)
+    d = si.Case(c.q, c.k, c.v, c.scale, "additive", add)
+    assert torch.equal(run_gpu(c), run_gpu(d))
+
+
+@pytest.mark.parametrize("lq", [1, 50])
+def test_fully_masked_row_is_zero(gpu_lib, lq):
+    c = si.make_case(1, 2, 1, lq, 90, 64, dtype="bf16", mask_kind="boolean", seed=2, mask_shape="qk", mask_p=0.0)
+    c.mask[0, 0, lq // 2, :] = 0
+    out = run_gpu(c)
+    assert torch.isfinite(out).all()
+    assert (out[:, :, lq // 2] == 0).all()
+    assert_parity(out, oracle_out(c), "bf16", "fully masked row")
+
+
+def test_f16_minus_1e9_becomes_minus_inf_without_nan(gpu_lib):
+    c = si.make_case(1, 8, 2, 1, 500, 128, dtype="f16", mask_kind="additive", seed=12, mask_p=0.5)
+    assert torch.isinf(c.mask.float()).any()
+    out = run_gpu(c)
+    assert torch.isfinite(out).all()
+    assert_parity(out, oracle_out(c), "f16", "f16 -inf additive")
+
+
+def test_single_key_and_large_scores(gpu_lib):
+    c = si.make_case(1, 2, 2, 20, 1, 64, dtype="f32", seed=1)
+    out = run_gpu(c).cpu()
+    assert torch.allclose(out, c.v.expand(1, 2, 20, 64), atol=0, rtol=0)
+    big = si.make_case(1, 2, 2, 20, 40, 64, dtype="f32", seed=1, std=30.0)
+    assert_parity(run_gpu(big), oracle_out(big), "f32", "large scores")
+
+
+def test_output_canary_untouched(gpu_lib):
+    import scaled_dot_product_sdpa_amd as sdpa
+    c = si.make_case(1, 4, 2, 33, 77, 72, dtype="bf16", mask_kind="causal", seed=6)
+    q, k, v, _ = to_device(c)
+    buf = torch.full((4096 + 1 * 4 * 33 * 72 + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[4096:4096 + 4 * 33 * 72].view(1, 4, 33, 72)
+    sdpa.forward(q, k, v, scale=c.scale, mask_kind="causal", out=out)
+    torch.cuda.synchronize()
+    assert (buf[:4096] == 7.0).all() and (buf[-4096:] == 7.0).all()
+    assert_parity(out, oracle_out(c), "bf16", "canary")
+
+
+def test_unsupported_shapes_raise_not_fall_back(gpu_lib):
+    import scaled_dot_product_sdpa_amd as sdpa
+    q = torch.zeros(1, 2, 16, 48, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sdpa.SdpaError) as e:
+        sdpa.forward(q, q, q)
+    assert e.value.status == -2
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 3, 16, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sdpa.SdpaError):
+        sdpa.forward(q, k, k)
+    # d stride != 1
+    x = torch.zeros(1, 2, 64, 16, dtype=torch.bfloat16, device="cuda").transpose(2, 3)
+    with pytest.raises(sdpa.SdpaError) as e:
+        sdpa.forward(x, x, x)
+    assert e.value.status == -2
+
+
+def test_no_score_tensor_is_materialised(gpu_lib):
+    """Peak memory growth of a prefill call stays at the output size (no [B,H,L,L] scores)."""
+    import scaled_dot_product_sdpa_amd as sdpa
+    c = si.prefill512_case(seq=4096)
+    q, k, v, _ = to_device(c)
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    sdpa.forward(q, k, v, scale=c.scale, mask_kind="causal", out=out)
+    torch.cuda.synchronize()
+    grown = torch.cuda.max_memory_allocated() - base
+    assert grown < (1 << 20), f"peak grew by {grown} bytes"

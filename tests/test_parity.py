@@ -1,0 +1,126 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Tolerances: float32 max abs <= 2e-5; float16 / bfloat16 max abs <= 2e-2 and
+relative L2 <= 1e-2.  Every failure message prints the measured error.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sdpa_inputs as si
+from gpu_util import DT_NAME, assert_parity, oracle_out, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+HEAD_DIMS = [64, 72, 80, 96, 128, 256, 512]
+DTYPES = ["f32", "f16", "bf16"]
+MASKS = ["none", "additive", "boolean", "causal"]
+
+
+# --------------------------------------------------------------------------
+# Tiny float32 configuration: B=2, L=82, H=8, D=64, both layouts.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["random", "linspace"])
+def test_tiny_f32_matches_oracle_in_both_layouts(gpu_lib, variant):
+    c = si.tiny_case(variant)
+    ref = oracle_out(c)
+    out = run_gpu(c)
+    assert_parity(out, ref, "f32", f"tiny-{variant}-blhd")
+    ct = si.tiny_case(variant, transposed=True)
+    out_t = run_gpu(ct)
+    assert_parity(out_t, ref, "f32", f"tiny-{variant}-bhld")
+    assert torch.equal(out, out_t), "layout permutation changed the output bits"
+
+
+def test_tiny_linspace_is_far_from_the_swapped_layout_result(gpu_lib):
+    """The page's bug read [B,L,H,D] as [B,H,L,D]; our output must sit at the correct answer."""
+    import oracle
+    c = si.tiny_case("linspace")
+    out = run_gpu(c).double().cpu().numpy()
+    a = si.linspace_block((2, 82, 8, 64)).astype(np.float64).reshape(-1)
+    swapped = oracle.sdpa_strided(a, (82 * 512, 512, 64, 1), a, (82 * 512, 512, 64, 1), a, (82 * 512, 512, 64, 1),
+                                  2, 8, 8, 82, 82, 64, float(np.float32(0.125)))
+    # compare in [B,L,H,D] positions
+    got_blhd = out.transpose(0, 2, 1, 3)
+    assert np.abs(got_blhd - swapped).max() > 0.2
+
+
+# --------------------------------------------------------------------------
+# Prefill matrix: every head dim x dtype x mask kind, several tiles + ragged tails, GQA.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("mask_kind", MASKS)
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("D", HEAD_DIMS)
+def test_prefill_matrix(gpu_lib, D, dtype, mask_kind):
+    c = si.make_case(2, 4, 2, 150, 150, D, dtype=dtype, layout="blhd", mask_kind=mask_kind,
+                     seed=D * 10 + MASKS.index(mask_kind), mask_shape="full" if mask_kind != "additive" else "qk",
+                     mask_p=0.2)
+    assert_parity(run_gpu(c), oracle_out(c), dtype, f"prefill D={D} {dtype} {mask_kind}")
+
+
+@pytest.mark.parametrize("lq,lk", [(9, 9), (40, 200), (130, 64), (300, 33), (64, 1)])
+@pytest.mark.parametrize("mask_kind", MASKS)
+def test_prefill_unequal_lengths(gpu_lib, lq, lk, mask_kind):
+    c = si.make_case(1, 6, 3, lq, lk, 72, dtype="bf16", layout="bhld", mask_kind=mask_kind, seed=lq + lk,
+                     mask_shape="qk", mask_p=0.2)
+    assert_parity(run_gpu(c), oracle_out(c), "bf16", f"prefill Lq={lq} Lk={lk} {mask_kind}")
+
+
+# --------------------------------------------------------------------------
+# Decode matrix (q_len <= 8 -> vector kernel, split keys + combine).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("lq", [1, 5])
+@pytest.mark.parametrize("mask_kind", MASKS)
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("D", HEAD_DIMS)
+def test_decode_matrix(gpu_lib, D, dtype, mask_kind, lq):
+    c = si.make_case(2, 8, 2, lq, 300, D, dtype=dtype, layout="bhld", mask_kind=mask_kind, seed=D + lq,
+                     mask_shape="full", mask_p=0.2)
+    assert_parity(run_gpu(c), oracle_out(c), dtype, f"decode D={D} {dtype} {mask_kind} Lq={lq}")
+
+
+@pytest.mark.parametrize("hq,hkv,lq", [(64, 1, 8), (40, 5, 8), (3, 3, 1), (16, 2, 8)])
+def test_decode_many_rows_per_group(gpu_lib, hq, hkv, lq):
+    """n_rep * q_len beyond one 32-column block uses several column groups."""
+    c = si.make_case(1, hq, hkv, lq, 257, 128, dtype="bf16", mask_kind="causal", seed=hq)
+    assert_parity(run_gpu(c), oracle_out(c), "bf16", f"decode Hq={hq} Hkv={hkv} Lq={lq}")
+
+
+# --------------------------------------------------------------------------
+# The benchmark configurations at their full sizes.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("lk", si.DECODE_LENGTHS)
+@pytest.mark.parametrize("D", [256, 512])
+def test_decode_configs_full_size(gpu_lib, D, lk):
+    c = si.decode_case(D, lk)
+    assert_parity(run_gpu(c), oracle_out(c), "bf16", c.name)
+
+
+SAMPLE_ROWS = [0, 1, 31, 32, 63, 64, 127, 128, 1000, 4095, 4096, 8190, 8191]
+
+
+@pytest.mark.parametrize("mask_kind", ["none", "boolean", "causal"])
+def test_prefill_d72_full_size_sampled_rows(gpu_lib, mask_kind):
+    c = si.prefill72_case(mask_kind)
+    out = run_gpu(c)
+    ref = oracle_out(c, q_rows=SAMPLE_ROWS)
+    assert_parity(out[:, :, SAMPLE_ROWS], ref, "bf16", c.name)
+
+
+def test_prefill_d72_reduced_seq_all_rows(gpu_lib):
+    for kind in ("none", "boolean", "causal"):
+        c = si.prefill72_case(kind, seq=700)
+        assert_parity(run_gpu(c), oracle_out(c), "bf16", c.name)
+
+
+def test_prefill_d512_full_size_sampled_rows(gpu_lib):
+    c = si.prefill512_case()
+    out = run_gpu(c)
+    rows = [0, 1, 31, 32, 100, 2047, 2048, 4000, 4095]
+    ref = oracle_out(c, q_rows=rows)
+    assert_parity(out[:, :, rows], ref, "bf16", c.name)
+
+
+def test_prefill_d512_reduced_seq_all_rows(gpu_lib):
+    c = si.prefill512_case(seq=300)
+    assert_parity(run_gpu(c), oracle_out(c), "bf16", c.name)
