@@ -185,6 +185,22 @@ int sdpa_last_hip_error(void);
  */
 int sdpa_route_counters(uint64_t* out, int n);
 
+/*
+ * Diagnostics: per-kernel timing with HIP events on the call's own stream.
+ * sdpa_timing_start(max_calls) creates 3 * max_calls events and arms the next
+ * max_calls calls of sdpa_forward made by this thread: each records an event
+ * before its first kernel and after each kernel it launches (the attention
+ * kernel, then the decode combine kernel when there is one).  Must not be
+ * active while a stream is being captured into a graph.
+ * sdpa_timing_stop(ms, cap) waits for the recorded events, writes
+ * ms[2*i] = attention-kernel milliseconds and ms[2*i+1] = combine-kernel
+ * milliseconds (0 for the full kernel) of call i, for at most cap/2 calls,
+ * destroys the events and returns the number of calls recorded (negative
+ * status on a HIP error).  Calls beyond max_calls are not recorded.
+ */
+int sdpa_timing_start(int max_calls);
+int sdpa_timing_stop(float* ms, int cap);
+
 #ifdef __cplusplus
 }
 #endif

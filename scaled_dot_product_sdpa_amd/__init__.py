@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     dtype_code,
     forward,
     head_dims,
+    kernel_timing,
     load,
     route_counters,
     select_kernel,

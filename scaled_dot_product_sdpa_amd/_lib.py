@@ -26,7 +26,8 @@ _TORCH_DT = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: S
 
 # Every symbol include/sdpa.h declares (checked by the CPU test suite).
 EXPORTS = ("sdpa_forward", "sdpa_select_kernel", "sdpa_describe_route", "sdpa_workspace_size",
-           "sdpa_head_dims", "sdpa_strerror", "sdpa_last_hip_error", "sdpa_route_counters")
+           "sdpa_head_dims", "sdpa_strerror", "sdpa_last_hip_error", "sdpa_route_counters",
+           "sdpa_timing_start", "sdpa_timing_stop")
 
 
 class Strides(ctypes.Structure):
@@ -71,6 +72,10 @@ def load(path: str = LIB_PATH):
         lib.sdpa_last_hip_error.restype = i
         lib.sdpa_route_counters.argtypes = [ctypes.POINTER(ctypes.c_uint64), i]
         lib.sdpa_route_counters.restype = i
+        lib.sdpa_timing_start.argtypes = [i]
+        lib.sdpa_timing_start.restype = i
+        lib.sdpa_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_float), i]
+        lib.sdpa_timing_stop.restype = i
         _lib = lib
         return lib
 
@@ -118,6 +123,31 @@ def route_counters() -> dict:
     arr = (ctypes.c_uint64 * 4)()
     load().sdpa_route_counters(arr, 4)
     return dict(zip(("calls", "full", "vector", "rejected"), (int(x) for x in arr)))
+
+
+class kernel_timing:
+    """Context manager: per-kernel milliseconds of the sdpa_forward calls made inside it.
+
+    with kernel_timing(n) as t: ...calls...;  t.ms -> [(attention_ms, combine_ms), ...]
+    """
+
+    def __init__(self, max_calls: int):
+        self.max_calls = max_calls
+        self.ms = []
+
+    def __enter__(self):
+        st = load().sdpa_timing_start(self.max_calls)
+        if st != 0:
+            raise SdpaError(st, "sdpa_timing_start")
+        return self
+
+    def __exit__(self, *exc):
+        buf = (ctypes.c_float * (2 * self.max_calls))()
+        n = load().sdpa_timing_stop(buf, len(buf))
+        if n < 0:
+            raise SdpaError(n, "sdpa_timing_stop")
+        self.ms = [(buf[2 * i], buf[2 * i + 1]) for i in range(n)]
+        return False
 
 
 def _as_code(dtype) -> int:

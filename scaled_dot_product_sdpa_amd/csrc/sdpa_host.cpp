@@ -18,6 +18,7 @@
 #include <mutex>
 #include <set>
 #include <string>
+#include <vector>
 
 #include "launch.h"
 
@@ -217,6 +218,17 @@ void log_route_once(const std::string& s) {
     if (seen.insert(s).second) std::fprintf(stderr, "[sdpa] %s\n", s.c_str());
 }
 
+// Event ring for sdpa_timing_start / sdpa_timing_stop (per thread).
+struct Timing {
+    std::vector<hipEvent_t> ev;  // 3 per call
+    std::vector<int> nkern;      // kernels recorded per call
+    int armed = 0;
+    int used = 0;
+};
+thread_local Timing g_timing;
+
+hipEvent_t timing_event(int call, int k) { return g_timing.ev[3 * call + k]; }
+
 int reject(int st) {
     g_counters[3].fetch_add(1, std::memory_order_relaxed);
     return st;
@@ -282,6 +294,46 @@ const char* sdpa_strerror(int status) {
 }
 
 int sdpa_last_hip_error(void) { return g_last_hip_error; }
+
+int sdpa_timing_start(int max_calls) {
+    float dummy;
+    if (!g_timing.ev.empty()) sdpa_timing_stop(&dummy, 0);
+    if (max_calls <= 0) return SDPA_EINVAL;
+    g_timing.ev.assign(3 * (size_t)max_calls, nullptr);
+    g_timing.nkern.assign(max_calls, 0);
+    for (auto& e : g_timing.ev) {
+        const hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) {
+            g_last_hip_error = (int)r;
+            return SDPA_EHIP;
+        }
+    }
+    g_timing.armed = max_calls;
+    g_timing.used = 0;
+    return SDPA_OK;
+}
+
+int sdpa_timing_stop(float* ms, int cap) {
+    int st = g_timing.used;
+    for (int i = 0; i < g_timing.used; ++i) {
+        for (int k = 0; k < 2; ++k) {
+            float t = 0.f;
+            if (k < g_timing.nkern[i]) {
+                hipError_t r = hipEventSynchronize(timing_event(i, k + 1));
+                if (r == hipSuccess) r = hipEventElapsedTime(&t, timing_event(i, k), timing_event(i, k + 1));
+                if (r != hipSuccess) {
+                    g_last_hip_error = (int)r;
+                    st = SDPA_EHIP;
+                }
+            }
+            if (ms && 2 * i + k < cap) ms[2 * i + k] = t;
+        }
+    }
+    for (auto e : g_timing.ev)
+        if (e) hipEventDestroy(e);
+    g_timing = Timing();
+    return st;
+}
 
 int sdpa_route_counters(uint64_t* out, int n) {
     for (int i = 0; out && i < n && i < 4; ++i) out[i] = g_counters[i].load(std::memory_order_relaxed);
@@ -357,6 +409,15 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     const KernelSet* ks = kernel_set(dtype, head_dim);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int mk = (int)mask_kind;
+    // optional per-kernel timing (diagnostics): events bracket each launch on `s`
+    int tcall = -1;
+    if (g_timing.used < g_timing.armed) tcall = g_timing.used++;
+    auto mark = [&](int k) {
+        if (tcall >= 0) {
+            hipEventRecord(timing_event(tcall, k), s);
+            g_timing.nkern[tcall] = k;
+        }
+    };
 
     if (kern == SDPA_KERNEL_FULL) {
         const auto& t = ks->full_cfg;
@@ -364,8 +425,10 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         dim3 grid((unsigned)((q_len + bm - 1) / bm), (unsigned)n_q_heads, (unsigned)batch);
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, st,
                                     kern, reason));
+        mark(0);
         st = hip_status(ks->full[mk](p, grid, s));
         if (st != SDPA_OK) return reject(st);
+        mark(1);
         g_counters[1].fetch_add(1, std::memory_order_relaxed);
         return SDPA_OK;
     }
@@ -388,11 +451,14 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, st, kern,
                                 reason));
     dim3 grid((unsigned)plan.splits, (unsigned)(n_kv_heads * plan.col_groups), (unsigned)batch);
+    mark(0);
     st = hip_status(ks->decode[mk](p, grid, s));
     if (st != SDPA_OK) return reject(st);
+    mark(1);
     dim3 cgrid((unsigned)rows, (unsigned)((head_dim + 255) / 256), 1);
     st = hip_status(ks->combine(p, cgrid, s));
     if (st != SDPA_OK) return reject(st);
+    mark(2);
     g_counters[2].fetch_add(1, std::memory_order_relaxed);
     return SDPA_OK;
 }

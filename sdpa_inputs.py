@@ -157,3 +157,14 @@ def prefill512_case(seq=4096, dtype="bf16") -> Case:
     """bf16 prefill B=1, Hq=32, Hkv=4, D=512, Lq=Lk=seq, causal, [B,H,L,D]."""
     return make_case(1, 32, 4, seq, seq, 512, dtype=dtype, layout="bhld", mask_kind="causal",
                      seed=5, name=f"prefill-d512-causal-L{seq}")
+
+
+def to_device(case: Case, device="cuda"):
+    """Copy a case's physical storage to `device`; return the same logical views (q, k, v, mask)."""
+    def dev(t):
+        if case.layout == "blhd":
+            return t.transpose(1, 2).contiguous().to(device).transpose(1, 2)
+        return t.contiguous().to(device)
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    mask = case.mask.to(device) if case.mask is not None else None
+    return q, k, v, mask

@@ -11,15 +11,7 @@ TOL = {"f32": dict(max_abs=2e-5, rel_l2=None), "f16": dict(max_abs=2e-2, rel_l2=
 DT_NAME = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
 
 
-def to_device(case: si.Case, device="cuda"):
-    """Copy a case's physical storage to the GPU and return the same logical views."""
-    def dev(t):
-        if case.layout == "blhd":
-            return t.transpose(1, 2).contiguous().to(device).transpose(1, 2)
-        return t.contiguous().to(device)
-    q, k, v = dev(case.q), dev(case.k), dev(case.v)
-    mask = case.mask.to(device) if case.mask is not None else None
-    return q, k, v, mask
+to_device = si.to_device
 
 
 def run_gpu(case: si.Case, **kw):
