@@ -34,7 +34,9 @@
  *     tensor has strides (L*H*D, D, H*D, 1); a [B,H,L,D] one (H*L*D, L*D, D, 1).
  *     The d stride must be 1.  For Q, K, V and O every other stride and the
  *     base address must be 16-byte aligned (a multiple of 8 elements for
- *     16-bit types, 4 for float32).
+ *     16-bit types, 4 for float32).  K and V rows may not overlap (row
+ *     stride >= head_dim when kv_len > 1) and kv_len * row stride of one
+ *     key/value head must stay below 4 GiB.
  *   - Grouped-query attention: Hq must be a multiple of Hkv; query head h
  *     reads key/value head h / (Hq / Hkv).
  *   - Device pointers are HIP device pointers on the current device; the

@@ -29,7 +29,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-enum { MASK_NONE = 0, MASK_ADD = 1, MASK_BOOL = 2, MASK_CAUSAL = 3 };
+// Kernel mask variants.  The C ABI's additive kind maps to MASK_ADD16
+// (bf16 / f16 mask) or MASK_ADD32 (float32 mask).
+enum { MASK_NONE = 0, MASK_ADD16 = 1, MASK_BOOL = 2, MASK_CAUSAL = 3, MASK_ADD32 = 4, MASK_VARIANTS = 5 };
 enum { MDT_F32 = 0, MDT_F16 = 1, MDT_BF16 = 2, MDT_U8 = 3 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -47,6 +49,7 @@ struct Params {
     int mask_vec;     // 1: key stride 1 and 4-element runs aligned -> vector loads
     int B, Lq, Lk, Hq, Hkv, n_rep;
     float scale_log2;  // scale * log2(e)
+    int scale_nonneg;  // scale >= 0: the row max can be taken on unscaled scores
     // vector (decode) kernel
     float* ws_o;      // [B*Hq*Lq][splits][D] unnormalised partial outputs
     float* ws_ml;     // [B*Hq*Lq][splits][2] running max (log2 domain) and sum
@@ -123,33 +126,69 @@ struct TF32 {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
-
-// Mask value for one (row, key) of an additive mask, widened to float.
-__device__ __forceinline__ float load_mask_scalar(const void* base, int64_t off, int mdt) {
-    if (mdt == MDT_F32) return reinterpret_cast<const float*>(base)[off];
-    uint16_t u = reinterpret_cast<const uint16_t*>(base)[off];
-    if (mdt == MDT_BF16) return __uint_as_float((uint32_t)u << 16);
-    return (float)bitcast<_Float16>(u);
+// Raw buffer resource over [base, base + bytes): a load whose 32-bit offset is
+// >= bytes returns zero without touching memory (hardware range check).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// Four consecutive keys of an additive mask (key stride 1, 4-element aligned run).
-__device__ __forceinline__ f32x4_t load_mask4(const void* base, int64_t off, int mdt) {
-    if (mdt == MDT_F32) return *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(base) + off);
-    u32x2_t w = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(base) + off);
-    f32x4_t r;
-    if (mdt == MDT_BF16) {
-        r[0] = __uint_as_float(w[0] << 16);
-        r[1] = __uint_as_float(w[0] & 0xffff0000u);
-        r[2] = __uint_as_float(w[1] << 16);
-        r[3] = __uint_as_float(w[1] & 0xffff0000u);
-    } else {
-        r[0] = (float)bitcast<_Float16>((uint16_t)(w[0] & 0xffffu));
-        r[1] = (float)bitcast<_Float16>((uint16_t)(w[0] >> 16));
-        r[2] = (float)bitcast<_Float16>((uint16_t)(w[1] & 0xffffu));
-        r[3] = (float)bitcast<_Float16>((uint16_t)(w[1] >> 16));
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// ---------------------------------------------------------------------------
+// Masks are read in groups of 4 consecutive keys (the 4 keys one lane holds
+// per accumulator group).  Raw form kept in registers until use:
+//   MASK_BOOL  : 1 dword, byte r = key r (nonzero = attend)
+//   MASK_ADD16 : 2 dwords, 16-bit values of keys 0..3 (bf16 or f16)
+//   MASK_ADD32 : 4 dwords, float32 values of keys 0..3
+// A tile's groups are loaded right after the previous tile's softmax, so the
+// load overlaps that tile's P V products and the next tile's Q K^T.
+// Keys >= Lk read as "masked" / 0 and are masked separately.
+// ---------------------------------------------------------------------------
+template <int MASK> struct MaskRaw { using type = uint32_t; };           // MASK_BOOL: 4 bytes
+template <> struct MaskRaw<MASK_ADD16> { using type = u32x2_t; };         // 4 x 16-bit
+template <> struct MaskRaw<MASK_ADD32> { using type = u32x4_t; };         // 4 x float32
+
+template <int MASK>
+__device__ __forceinline__ typename MaskRaw<MASK>::type load_mask_group(const Params& p, int64_t mrow, int key0) {
+    using R = typename MaskRaw<MASK>::type;
+    const char* base = reinterpret_cast<const char*>(p.mask);
+    if (p.mask_vec && key0 + 3 < p.Lk) {
+        if constexpr (MASK == MASK_BOOL) return *reinterpret_cast<const uint32_t*>(base + mrow + key0);
+        else if constexpr (MASK == MASK_ADD16) return *reinterpret_cast<const u32x2_t*>(base + (mrow + key0) * 2);
+        else return *reinterpret_cast<const u32x4_t*>(base + (mrow + key0) * 4);
+    }
+    R r{};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int j = key0 + k;
+        if (j >= p.Lk) continue;
+        const int64_t o = mrow + (int64_t)j * p.ms[3];
+        if constexpr (MASK == MASK_BOOL) {
+            r |= (base[o] ? 1u : 0u) << (8 * k);
+        } else if constexpr (MASK == MASK_ADD16) {
+            const uint32_t u = reinterpret_cast<const uint16_t*>(base)[o];
+            r[k >> 1] |= u << (16 * (k & 1));
+        } else {
+            r[k] = reinterpret_cast<const uint32_t*>(base)[o];
+        }
     }
     return r;
+}
+
+// Additive mask value of key k (0..3) of a raw group, widened to float.
+template <int MASK>
+__device__ __forceinline__ float mask_value(const typename MaskRaw<MASK>::type& r, int k, int mdt) {
+    if constexpr (MASK == MASK_ADD32) {
+        return __uint_as_float(r[k]);
+    } else {
+        const uint32_t w = r[k >> 1];
+        const uint32_t h = (k & 1) ? (w >> 16) : (w & 0xffffu);
+        if (mdt == MDT_BF16) return __uint_as_float(h << 16);
+        return (float)bitcast<_Float16>((uint16_t)h);
+    }
 }
 
 }  // namespace sdpa_dev

@@ -26,20 +26,28 @@
 //     are zero-padded in LDS and in the Q fragments; when D % 32 != 0 the V^T
 //     tile has spare rows and row D is set to ones, so the MFMA produces the
 //     softmax row sums along with O (already rescaled with it).
-//   * Prefill grid: (query tiles, Hq, B); causal launches the longest tiles
-//     first and stops at the diagonal (bottom-right aligned).  Decode grid:
-//     (key splits, Hkv * column groups, B); a column enumerates
-//     (query head in the group, query row), so all n_rep query heads of a
-//     key/value head share every K/V byte read.
+//   * Prefill grid: one dimension, 8 x ceil(items / 8) workgroups, items =
+//     (batch, query head, query tile).  Workgroup i runs on XCD i % 8, so
+//     XCD x is given the contiguous item range [x * per, (x + 1) * per): the
+//     query tiles of one head run on one XCD and share its L2 copy of that
+//     head's K/V.  Causal items run longest-first and stop at the diagonal
+//     (bottom-right aligned).  Decode grid: (key splits, Hkv * column groups,
+//     B); a column enumerates (query head in the group, query row), so all
+//     n_rep query heads of a key/value head share every K/V byte read.
+//   * Softmax per tile: full tiles without a per-element mask take the row
+//     max on unscaled scores and need one FMA and one exp2 per score; the
+//     output is rescaled only when a row max grows by more than 2^8
+//     (otherwise the stale max is kept, so probabilities stay <= 2^8).
 #pragma once
 
 #include "attn_common.h"
 
 namespace sdpa_dev {
 
-template <class TR, int D_, int BN_, int WM_, int WD_>
+template <class TR, int D_, int BN_, int WM_, int WD_, int OCC_ = 1>
 struct TileCfg {
     static constexpr int D = D_, BN = BN_, WM = WM_, WD = WD_;
+    static constexpr int OCC = OCC_;  // minimum waves per SIMD the register budget must allow
     static constexpr int NW = WM * WD, NT = 64 * NW;
     static constexpr int ES = TR::ES, EPC = TR::EPC, KCH = TR::KCH;
     static constexpr int DW = D / WD;
@@ -72,9 +80,12 @@ template <> struct OneBits<TF16> { static constexpr uint32_t v = 0x3C00u; };
 template <> struct OneBits<TF32> { static constexpr uint32_t v = 0x3F800000u; };
 
 template <class TR, class C, int MASK, bool DECODE>
-__global__ __launch_bounds__(C::NT) void attn_tile_kernel(const Params p) {
+__global__ __launch_bounds__(C::NT, C::OCC) void attn_tile_kernel(const Params p) {
     constexpr int ES = C::ES, EPC = C::EPC, KCH = C::KCH, BN = C::BN, D = C::D, DW = C::DW;
+    constexpr int BM = 32 * C::WM;
     constexpr float NEG_INF = -__builtin_inff();
+    constexpr float kRescale = 8.0f;  // log2 units
+    constexpr bool HAS_MT = (MASK == MASK_ADD16 || MASK == MASK_ADD32 || MASK == MASK_BOOL);
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
     char* const Ks = smem;
     char* const Vt = smem + C::LDS_K;
@@ -83,35 +94,43 @@ __global__ __launch_bounds__(C::NT) void attn_tile_kernel(const Params p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WD, wd = wave % C::WD;
     const int col = lane & 31, hh = lane >> 5;
-    const int b = blockIdx.z;
 
     // ---- columns -> (query head, query row); key range of this workgroup ----
-    int g, qh, qi, split = 0;
+    int b, g, qh, qi, split = 0, qmin;
     bool rv;
     int kbeg, kend;
     if constexpr (!DECODE) {
-        int t = blockIdx.x;
-        if (MASK == MASK_CAUSAL) t = (int)gridDim.x - 1 - t;  // longest causal tiles first
-        qh = blockIdx.y;
+        const int nqt = (p.Lq + BM - 1) / BM;
+        const int total = nqt * p.Hq * p.B;
+        const int per = (total + 7) / 8;
+        const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+        if (item >= total) return;  // whole workgroup: no barrier is skipped
+        const int tt = item % nqt, bh = item / nqt;
+        qh = bh % p.Hq;
+        b = bh / p.Hq;
+        const int t = (MASK == MASK_CAUSAL) ? nqt - 1 - tt : tt;
         g = qh / p.n_rep;
-        const int i0 = t * 32 * C::WM;
-        qi = i0 + 32 * wm + col;
+        const int i0 = t * BM;
+        qmin = i0 + 32 * wm;
+        qi = qmin + col;
         rv = qi < p.Lq;
         kbeg = 0;
         kend = p.Lk;
         if (MASK == MASK_CAUSAL) {
-            const int64_t e = (int64_t)i0 + 32 * C::WM + (p.Lk - p.Lq);
+            const int64_t e = (int64_t)i0 + BM + (p.Lk - p.Lq);
             kend = (int)(e < 0 ? 0 : (e > p.Lk ? p.Lk : e));
         }
     } else {
+        b = blockIdx.z;
         split = blockIdx.x;
         g = blockIdx.y / p.col_groups;
         const int cg = blockIdx.y % p.col_groups;
-        const int r = cg * 32 * C::WM + 32 * wm + col;
+        const int r = cg * BM + 32 * wm + col;
         rv = r < p.n_rep * p.Lq;
         const int rr = rv ? r : 0;
         qh = g * p.n_rep + rr / p.Lq;
         qi = rr % p.Lq;
+        qmin = 0;
         kbeg = split * p.keys_per_split;
         kend = min(p.Lk, kbeg + p.keys_per_split);
     }
@@ -120,6 +139,7 @@ __global__ __launch_bounds__(C::NT) void attn_tile_kernel(const Params p) {
                               ((int64_t)b * p.ks[0] + (int64_t)g * p.ks[1]) * ES;
     const char* const vglob = reinterpret_cast<const char*>(p.v) +
                               ((int64_t)b * p.vs[0] + (int64_t)g * p.vs[1]) * ES;
+    const int64_t kstep = (int64_t)p.ks[2] * ES, vstep = (int64_t)p.vs[2] * ES;
 
     // ---- Q fragments (MFMA B operand), zero beyond D / beyond the rows ----
     u32x4_t qf[C::NCH];
@@ -152,87 +172,104 @@ __global__ __launch_bounds__(C::NT) void attn_tile_kernel(const Params p) {
         }
     }
 
-    // ---- tile loader: global -> registers, registers -> LDS ----
+    // ---- per-thread load slots: byte offsets from the (batch, kv head) base ----
+    // K and V are read through buffer resources that end with the last byte of
+    // key kend - 1, so rows past the keys of this workgroup read as zero (the
+    // host guarantees row stride >= D whenever there is more than one key).
+    const uint32_t kstep32 = (uint32_t)kstep, vstep32 = (uint32_t)vstep;
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc(kglob, kend > 0 ? (uint32_t)(kend - 1) * kstep32 + (uint32_t)(D * ES) : 0u);
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc(vglob, kend > 0 ? (uint32_t)(kend - 1) * vstep32 + (uint32_t)(D * ES) : 0u);
+    bool kok[C::UK], vok[C::UV];
+    uint32_t koff[C::UK], voff[C::UV];
+    int klds[C::UK], vlds[C::UV], vq[C::UV];
+#pragma unroll
+    for (int u = 0; u < C::UK; ++u) {
+        const int idx = tid + u * C::NT;
+        const int key = idx / C::KCPR, c = idx % C::KCPR;
+        kok[u] = idx < BN * C::KCPR;
+        koff[u] = (uint32_t)key * kstep32 + (uint32_t)(c * 16);
+        klds[u] = (key * C::KP + c * EPC) * ES;
+    }
+#pragma unroll
+    for (int u = 0; u < C::UV; ++u) {
+        const int idx = tid + u * C::NT;
+        const int q4 = idx / C::KCPR, c = idx % C::KCPR;
+        vok[u] = idx < (BN / 4) * C::KCPR;
+        voff[u] = (uint32_t)(4 * q4) * vstep32 + (uint32_t)(c * 16);
+        vq[u] = 4 * q4;
+        vlds[u] = c * EPC;  // first d of the chunk; LDS row = d, column = 4 * q4
+    }
+
+    // mask row of this lane's query (row 0 for padding columns: never used)
+    const int64_t mrow = HAS_MT ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)(rv ? qi : 0) * p.ms[2] : 0;
+
     u32x4_t kr[C::UK];
     u32x4_t vr[C::UV][4];
+    typename MaskRaw<MASK>::type mr[HAS_MT ? C::NKB : 1][4];
+    auto load_mask = [&](int kt) {
+        if constexpr (HAS_MT) {
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) mr[kb][a4] = load_mask_group<MASK>(p, mrow, kt + kb * 32 + 8 * a4 + 4 * hh);
+        }
+    };
     auto load_tile = [&](int kt) {
+        const uint32_t kb0 = (uint32_t)kt * kstep32, vb0 = (uint32_t)kt * vstep32;
 #pragma unroll
-        for (int u = 0; u < C::UK; ++u) {
-            const int idx = tid + u * C::NT;
-            kr[u] = u32x4_t{0u, 0u, 0u, 0u};
-            if (idx < BN * C::KCPR) {
-                const int key = idx / C::KCPR, c = idx % C::KCPR;
-                const int j = kt + key;
-                if (j < kend)
-                    kr[u] = *reinterpret_cast<const u32x4_t*>(kglob + ((int64_t)j * p.ks[2] + c * EPC) * ES);
+        for (int u = 0; u < C::UK; ++u)
+            if (kok[u]) kr[u] = buffer_load16(krs, koff[u] + kb0);
+#pragma unroll
+        for (int u = 0; u < C::UV; ++u)
+            if (vok[u]) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) vr[u][r] = buffer_load16(vrs, voff[u] + vb0 + (uint32_t)r * vstep32);
             }
-        }
-#pragma unroll
-        for (int u = 0; u < C::UV; ++u) {
-            const int idx = tid + u * C::NT;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) vr[u][r] = u32x4_t{0u, 0u, 0u, 0u};
-            if (idx < (BN / 4) * C::KCPR) {
-                const int q4 = idx / C::KCPR, c = idx % C::KCPR;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = kt + 4 * q4 + r;
-                    if (j < kend)
-                        vr[u][r] = *reinterpret_cast<const u32x4_t*>(vglob + ((int64_t)j * p.vs[2] + c * EPC) * ES);
-                }
-            }
-        }
     };
     auto store_tile = [&]() {
 #pragma unroll
-        for (int u = 0; u < C::UK; ++u) {
-            const int idx = tid + u * C::NT;
-            if (idx < BN * C::KCPR) {
-                const int key = idx / C::KCPR, c = idx % C::KCPR;
-                *reinterpret_cast<u32x4_t*>(Ks + (key * C::KP + c * EPC) * ES) = kr[u];
-            }
-        }
+        for (int u = 0; u < C::UK; ++u)
+            if (kok[u]) *reinterpret_cast<u32x4_t*>(Ks + klds[u]) = kr[u];
 #pragma unroll
         for (int u = 0; u < C::UV; ++u) {
-            const int idx = tid + u * C::NT;
-            if (idx < (BN / 4) * C::KCPR) {
-                const int q4 = idx / C::KCPR, c = idx % C::KCPR;
-                if constexpr (ES == 2) {
-                    // 4 keys x 8 d -> 8 rows of V^T, 4 keys (8 bytes) each
+            if (!vok[u]) continue;
+            const int q0 = vq[u], d0 = vlds[u];
+            if constexpr (ES == 2) {
+                // 4 keys x 8 d -> 8 rows of V^T, 4 keys (8 bytes) each
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) {
+                for (int w = 0; w < 4; ++w) {
 #pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            const uint32_t sel = e ? 0x07060302u : 0x05040100u;
-                            const uint32_t lo = __builtin_amdgcn_perm(vr[u][1][w], vr[u][0][w], sel);
-                            const uint32_t hi = __builtin_amdgcn_perm(vr[u][3][w], vr[u][2][w], sel);
-                            const int d = c * 8 + 2 * w + e;
-                            *reinterpret_cast<u32x2_t*>(Vt + (d * C::VP + 4 * q4) * 2) = u32x2_t{lo, hi};
-                        }
+                    for (int e = 0; e < 2; ++e) {
+                        const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+                        const uint32_t lo = __builtin_amdgcn_perm(vr[u][1][w], vr[u][0][w], sel);
+                        const uint32_t hi = __builtin_amdgcn_perm(vr[u][3][w], vr[u][2][w], sel);
+                        const int d = d0 + 2 * w + e;
+                        *reinterpret_cast<u32x2_t*>(Vt + (d * C::VP + q0) * 2) = u32x2_t{lo, hi};
                     }
-                } else {
+                }
+            } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int d = c * 4 + i;
-                        *reinterpret_cast<u32x4_t*>(Vt + (d * C::VP + 4 * q4) * 4) =
-                            u32x4_t{vr[u][0][i], vr[u][1][i], vr[u][2][i], vr[u][3][i]};
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int d = d0 + i;
+                    *reinterpret_cast<u32x4_t*>(Vt + (d * C::VP + q0) * 4) =
+                        u32x4_t{vr[u][0][i], vr[u][1][i], vr[u][2][i], vr[u][3][i]};
                 }
             }
         }
     };
-
-    // mask row of this lane's query (row 0 for padding columns: never used)
-    const int64_t mrow = (MASK == MASK_ADD || MASK == MASK_BOOL)
-                             ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)(rv ? qi : 0) * p.ms[2]
-                             : 0;
 
     float m_run = NEG_INF, l_run = 0.f;
     f32x16_t oacc[C::NDB];
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16_t{};
+    const float c_scale = p.scale_log2;
 
-    if (kbeg < kend) load_tile(kbeg);
+    if (kbeg < kend) {
+        load_tile(kbeg);
+        load_mask(kbeg);
+    }
     for (int kt = kbeg; kt < kend; kt += BN) {
         __syncthreads();  // every wave is done reading the previous tile
         store_tile();
@@ -269,66 +306,66 @@ __global__ __launch_bounds__(C::NT) void attn_tile_kernel(const Params p) {
                 }
         }
 
-        // ---- mask, running max ----
-        float mloc = NEG_INF;
+        // ---- tile max; per-element masking only where needed (wave-uniform test) ----
+        const bool plain = !HAS_MT && p.scale_nonneg && (kt + BN <= kend) &&
+                           (MASK != MASK_CAUSAL || kt + BN - 1 <= qmin + off);
+        float mtile = NEG_INF;
+        float c_eff;
+        if (plain) {
+            float mx = NEG_INF;
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
+            for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int key0 = kt + kb * 32 + 8 * a4 + 4 * hh;
-                f32x4_t madd = {0.f, 0.f, 0.f, 0.f};
-                uint32_t mbits = 0x01010101u;
-                if constexpr (MASK == MASK_ADD || MASK == MASK_BOOL) {
-                    if (p.mask_vec && key0 + 3 < p.Lk) {
-                        if constexpr (MASK == MASK_ADD) madd = load_mask4(p.mask, mrow + key0, p.mask_dtype);
-                        else mbits = *reinterpret_cast<const uint32_t*>(
-                                 reinterpret_cast<const uint8_t*>(p.mask) + mrow + key0);
-                    } else {
-                        mbits = 0;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+            mtile = mx * c_scale;
+            c_eff = c_scale;
+        } else {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = key0 + r;
-                            if (j < p.Lk) {
-                                const int64_t o = mrow + (int64_t)j * p.ms[3];
-                                if constexpr (MASK == MASK_ADD) madd[r] = load_mask_scalar(p.mask, o, p.mask_dtype);
-                                else mbits |= (reinterpret_cast<const uint8_t*>(p.mask)[o] ? 1u : 0u) << (8 * r);
-                            }
-                        }
+            for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = kt + kb * 32 + 8 * a4 + 4 * hh + r;
+                        float x = sacc[kb][4 * a4 + r] * c_scale;
+                        bool ok = j < kend;
+                        if constexpr (MASK == MASK_ADD16 || MASK == MASK_ADD32)
+                            x = __builtin_fmaf(mask_value<MASK>(mr[kb][a4], r, p.mask_dtype), kLog2e, x);
+                        if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
+                        if constexpr (MASK == MASK_BOOL) ok = ok && ((mr[kb][a4] >> (8 * r)) & 0xffu) != 0u;
+                        x = ok ? x : NEG_INF;
+                        sacc[kb][4 * a4 + r] = x;
+                        mtile = fmaxf(mtile, x);
                     }
                 }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = key0 + r;
-                    float x = sacc[kb][4 * a4 + r] * p.scale_log2;
-                    if constexpr (MASK == MASK_ADD) x = __builtin_fmaf(madd[r], kLog2e, x);
-                    bool ok = j < kend;
-                    if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
-                    if constexpr (MASK == MASK_BOOL) ok = ok && ((mbits >> (8 * r)) & 0xffu) != 0u;
-                    x = ok ? x : NEG_INF;
-                    sacc[kb][4 * a4 + r] = x;
-                    mloc = fmaxf(mloc, x);
-                }
             }
+            c_eff = 1.f;
         }
-        mloc = fmaxf(mloc, xor32(mloc));
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
-        const float muse = (m_new == NEG_INF) ? 0.f : m_new;
+        mtile = fmaxf(mtile, xor32(mtile));
+        if (kt + BN < kend) load_mask(kt + BN);  // this tile's mask is consumed
+
+        // ---- online softmax: rescale only when some row max grows by > 2^8 ----
+        if (__any(mtile > m_run + kRescale)) {
+            const float m_new = fmaxf(m_run, mtile);
+            const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        const float muse = (m_run == NEG_INF) ? 0.f : m_run;
         float lsum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float e = fast_exp2(sacc[kb][r] - muse);
+                const float e = fast_exp2(__builtin_fmaf(sacc[kb][r], c_eff, -muse));
                 sacc[kb][r] = e;
                 lsum += e;
             }
-        if constexpr (!C::ONES) l_run = l_run * alpha + lsum;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        if constexpr (!C::ONES) l_run += lsum;
 
         // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -412,35 +449,53 @@ __global__ __launch_bounds__(C::NT) void attn_tile_kernel(const Params p) {
     }
 }
 
-// Decode combine: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, splits in
-// ascending order (deterministic).  grid = (B*Hq*Lq, ceil(D/256)), 256 threads.
+// Decode combine: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s over the
+// splits in ascending order (deterministic).  One wave per (output row,
+// 64-wide slice of d): grid = (B*Hq*Lq, ceil(D/64)).  The wave first turns the
+// split maxima into weights in LDS, then each lane accumulates one d.
+constexpr int kMaxSplits = 1024;
+
 template <class TR, int D>
-__global__ __launch_bounds__(256) void combine_kernel(const Params p) {
-    constexpr int ES = TR::ES;
+__global__ __launch_bounds__(64) void combine_kernel(const Params p) {
     constexpr float NEG_INF = -__builtin_inff();
+    __shared__ float wts[kMaxSplits];
     const int64_t row = blockIdx.x;
-    const int d = blockIdx.y * 256 + threadIdx.x;
+    const int lane = threadIdx.x;
     const int S = p.splits;
     const float* ml = p.ws_ml + row * S * 2;
     float M = NEG_INF;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-    if (d >= D) return;
-    float num = 0.f, den = 0.f;
-    if (M != NEG_INF) {
-        const float* po = p.ws_o + row * S * D + d;
-        for (int s = 0; s < S; ++s) {
-            const float ms = ml[2 * s];
-            const float w = (ms == NEG_INF) ? 0.f : fast_exp2(ms - M);
-            num = __builtin_fmaf(w, po[(int64_t)s * D], num);
-            den = __builtin_fmaf(w, ml[2 * s + 1], den);
-        }
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float den = 0.f;
+    for (int s = lane; s < S; s += 64) {
+        const float ms = ml[2 * s];
+        const float w = (ms == NEG_INF) ? 0.f : fast_exp2(ms - M);
+        wts[s] = w;
+        den = __builtin_fmaf(w, ml[2 * s + 1], den);
     }
-    const float val = den > 0.f ? num / den : 0.f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
+    __syncthreads();
+    const int d = blockIdx.y * 64 + lane;
+    if (d >= D) return;
+    const float* po = p.ws_o + row * S * D + d;
+    float num = 0.f;
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = po[(int64_t)(s + k) * D];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) num = __builtin_fmaf(wts[s + k], v[k], num);
+    }
+    for (; s < S; ++s) num = __builtin_fmaf(wts[s], po[(int64_t)s * D], num);
+    const float val = (M != NEG_INF && den > 0.f) ? num / den : 0.f;
     const int qi = (int)(row % p.Lq);
     const int64_t bh = row / p.Lq;
     const int qh = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
     char* dst = reinterpret_cast<char*>(p.o) +
-                ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2] + d) * ES;
+                ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2] + d) * TR::ES;
     TR::store1(dst, val);
 }
 

@@ -21,8 +21,8 @@ struct TileInfo {
 };
 
 struct KernelSet {
-    launch_fn full[4];    // indexed by mask kind
-    launch_fn decode[4];  // indexed by mask kind
+    launch_fn full[sdpa_dev::MASK_VARIANTS];    // indexed by kernel mask variant (MASK_*)
+    launch_fn decode[sdpa_dev::MASK_VARIANTS];  // indexed by kernel mask variant (MASK_*)
     launch_fn combine;
     TileInfo full_cfg;
     TileInfo dec_cfg;

@@ -20,6 +20,7 @@
 #include <string>
 #include <vector>
 
+#include "attn_kernel.h"
 #include "launch.h"
 
 using sdpa_dev::Params;
@@ -120,6 +121,7 @@ DecodePlan decode_plan(int batch, int q_len, int kv_len, int hq, int hkv, const 
     }
     if (s < 1) s = 1;
     if (s > max_splits) s = max_splits;
+    if (s > sdpa_dev::kMaxSplits) s = sdpa_dev::kMaxSplits;
     const int per = (int)((kv_len + s - 1) / s);
     p.keys_per_split = ((per + t.bn - 1) / t.bn) * t.bn;
     p.splits = (kv_len + p.keys_per_split - 1) / p.keys_per_split;
@@ -330,7 +332,7 @@ int sdpa_timing_stop(float* ms, int cap) {
         }
     }
     for (auto e : g_timing.ev)
-        if (e) hipEventDestroy(e);
+        if (e) (void)hipEventDestroy(e);
     g_timing = Timing();
     return st;
 }
@@ -359,6 +361,12 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     if ((st = check_operand(k, k_st, nk, es)) != SDPA_OK) return reject(st);
     if ((st = check_operand(v, v_st, nk, es)) != SDPA_OK) return reject(st);
     if ((st = check_operand(out, o_st, nq, es)) != SDPA_OK) return reject(st);
+    // K/V rows are read through 32-bit buffer offsets from each (batch, kv head)
+    // base: rows may not overlap and one head's keys must span < 4 GiB.
+    if (kv_len > 1 && (k_st.l < head_dim || v_st.l < head_dim)) return reject(SDPA_EUNSUPPORTED);
+    if ((double)kv_len * (double)(k_st.l > 0 ? k_st.l : 1) * es >= 4294967296.0 ||
+        (double)kv_len * (double)(v_st.l > 0 ? v_st.l : 1) * es >= 4294967296.0)
+        return reject(SDPA_EUNSUPPORTED);
     const size_t oq = span_bytes(nq, o_st, es);
     if (overlaps(out, oq, q, span_bytes(nq, q_st, es)) || overlaps(out, oq, k, span_bytes(nk, k_st, es)) ||
         overlaps(out, oq, v, span_bytes(nk, v_st, es)))
@@ -405,16 +413,19 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     p.Hkv = n_kv_heads;
     p.n_rep = n_q_heads / n_kv_heads;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    p.scale_nonneg = scale >= 0.f;
 
     const KernelSet* ks = kernel_set(dtype, head_dim);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const int mk = (int)mask_kind;
+    // kernel mask variant: the additive kind splits by mask element width
+    int mk = (int)mask_kind;
+    if (mask_kind == SDPA_MASK_ADDITIVE) mk = (mask_dtype == SDPA_F32) ? sdpa_dev::MASK_ADD32 : sdpa_dev::MASK_ADD16;
     // optional per-kernel timing (diagnostics): events bracket each launch on `s`
     int tcall = -1;
     if (g_timing.used < g_timing.armed) tcall = g_timing.used++;
     auto mark = [&](int k) {
         if (tcall >= 0) {
-            hipEventRecord(timing_event(tcall, k), s);
+            (void)hipEventRecord(timing_event(tcall, k), s);
             g_timing.nkern[tcall] = k;
         }
     };
@@ -422,7 +433,10 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     if (kern == SDPA_KERNEL_FULL) {
         const auto& t = ks->full_cfg;
         const int bm = 32 * t.wm;
-        dim3 grid((unsigned)((q_len + bm - 1) / bm), (unsigned)n_q_heads, (unsigned)batch);
+        // one-dimensional grid: 8 XCDs x ceil(items / 8), items = (batch, head, query tile)
+        const long items = (long)((q_len + bm - 1) / bm) * n_q_heads * batch;
+        if (items > (1L << 30)) return reject(SDPA_EUNSUPPORTED);
+        dim3 grid((unsigned)(8 * ((items + 7) / 8)), 1, 1);
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, st,
                                     kern, reason));
         mark(0);
@@ -455,7 +469,7 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     st = hip_status(ks->decode[mk](p, grid, s));
     if (st != SDPA_OK) return reject(st);
     mark(1);
-    dim3 cgrid((unsigned)rows, (unsigned)((head_dim + 255) / 256), 1);
+    dim3 cgrid((unsigned)rows, (unsigned)((head_dim + 63) / 64), 1);
     st = hip_status(ks->combine(p, cgrid, s));
     if (st != SDPA_OK) return reject(st);
     mark(2);

@@ -9,8 +9,10 @@ namespace sdpa_dev {
 
 // Prefill ("full"): 4 waves x 32 query rows for D <= 128; D = 256 splits the
 // head dim over 2 waves and D = 512 over 4 waves per 32-row block.
-template <class TR, int D> struct FullCfg { using type = TileCfg<TR, D, 64, 4, 1>; };
+template <class TR, int D> struct FullCfg { using type = TileCfg<TR, D, 64, 4, 1, 2>; };
+template <int D> struct FullCfg<TF32, D> { using type = TileCfg<TF32, D, 64, 4, 1, 1>; };
 template <class TR> struct FullCfg<TR, 256> { using type = TileCfg<TR, 256, 32, 2, 2>; };
+template <> struct FullCfg<TF32, 256> { using type = TileCfg<TF32, 256, 32, 2, 2>; };
 template <class TR> struct FullCfg<TR, 512> { using type = TileCfg<TR, 512, 32, 2, 4>; };
 template <> struct FullCfg<TF32, 512> { using type = TileCfg<TF32, 512, 32, 1, 4>; };
 
