@@ -1,0 +1,230 @@
+// Split-key decode ("vector") kernel for 16-bit inputs on gfx950.
+//
+// Decode (q_len <= 8, mlx issue #3885: "vector" kernel, and its 2-pass
+// variant that splits the keys over nkv x blocks threadgroups before a
+// combine) is bound by reading K and V once from HBM.  One workgroup handles
+// one (batch, kv head, key split) and all n_rep x q_len query rows of that kv
+// head (up to 16 per column group), so every K/V byte serves every query head
+// of its group.  Per chunk of KS = 16 * NW keys:
+//   1. all K and V loads of the chunk are issued at once: each wave loads the
+//      K rows of its 16 keys straight into v_mfma_f32_16x16x32 A-operand
+//      registers (lane l: key l % 16, head-dim columns 32 i + 8 (l / 16) .. +7)
+//      and its V rows into registers bound for LDS;
+//   2. S^T = K Q^T on the matrix cores (16 keys x 16 query rows per wave);
+//   3. exact softmax statistics of the chunk: row maxima and sums reduced
+//      over lanes (shuffles) and over waves (LDS); the chunk is merged into
+//      the running state with the usual 2^(m_old - m_new) rescale;
+//   4. P (rounded to the input type) goes to LDS; O^T += V^T P^T on the matrix
+//      cores, each wave owning every NW-th 16-column block of the head dim
+//      and reading V^T columns out of the row-major LDS copy.
+// The workgroup writes its unnormalised partial output, running max (log2
+// domain) and sum; combine_kernel merges the splits.
+#pragma once
+
+#include "attn_common.h"
+
+namespace sdpa_dev {
+
+template <class TR> struct Mma16;
+template <> struct Mma16<TBF16> {
+    static __device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
+    }
+};
+template <> struct Mma16<TF16> {
+    static __device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
+    }
+};
+
+template <class TR, int D_, int NW_>
+struct DecCfg {
+    static constexpr int D = D_, NW = NW_, NT = 64 * NW;
+    static constexpr int KS = 16 * NW;               // keys per chunk
+    static constexpr int NCH = (D + 31) / 32;        // Q K^T steps (32 head-dim columns each)
+    static constexpr int DV = (D + 15) / 16 * 16;    // V columns incl. zero pad
+    static constexpr int NDB = DV / 16;              // 16-column O^T blocks
+    static constexpr int NDBW = (NDB + NW - 1) / NW; // blocks per wave (round robin)
+    static constexpr int VP = DV + 4;                // V row pitch (elements): rows 8 apart land 64 B apart
+    static constexpr int PP = KS + 8;                // P row pitch (elements)
+    static constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
+    static constexpr int VU = (16 * CPR + 63) / 64;  // V chunks per lane
+    static constexpr int LDS = KS * VP * 2 + 16 * PP * 2 + 2 * NW * 16 * 4;
+    static_assert(D % 8 == 0, "head dim must be a whole number of 16-byte chunks");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <class TR, class C, int MASK>
+__global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
+    constexpr int D = C::D, NW = C::NW, KS = C::KS;
+    constexpr float NEG_INF = -__builtin_inff();
+    constexpr bool HAS_MT = (MASK == MASK_ADD16 || MASK == MASK_ADD32 || MASK == MASK_BOOL);
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[KS * C::VP];
+    __shared__ __attribute__((aligned(16))) uint16_t Ps[16 * C::PP];
+    __shared__ float red[2][NW][16];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int b = blockIdx.z, split = blockIdx.x;
+    const int grp = blockIdx.y / p.col_groups, cg = blockIdx.y % p.col_groups;
+    const int r = cg * 16 + col;
+    const bool rv = r < p.n_rep * p.Lq;
+    const int rr = rv ? r : 0;
+    const int qh = grp * p.n_rep + rr / p.Lq, qi = rr % p.Lq;
+    const int kbeg = split * p.keys_per_split;
+    const int kend = min(p.Lk, kbeg + p.keys_per_split);
+    const int off = p.Lk - p.Lq;
+
+    const int64_t kstep = p.ks[2] * 2, vstep = p.vs[2] * 2;
+    const char* kglob = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)grp * p.ks[1]) * 2;
+    const char* vglob = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)grp * p.vs[1]) * 2;
+    const uint32_t kstep32 = (uint32_t)kstep, vstep32 = (uint32_t)vstep;
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc(kglob, kend > 0 ? (uint32_t)(kend - 1) * kstep32 + (uint32_t)(D * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc(vglob, kend > 0 ? (uint32_t)(kend - 1) * vstep32 + (uint32_t)(D * 2) : 0u);
+
+    // Q fragments (B operand): row col, head-dim columns 32 i + 8 g .. +7
+    u32x4_t qf[C::NCH];
+    {
+        const char* qrow = reinterpret_cast<const char*>(p.q) +
+                           ((int64_t)b * p.qs[0] + (int64_t)qh * p.qs[1] + (int64_t)qi * p.qs[2]) * 2;
+#pragma unroll
+        for (int i = 0; i < C::NCH; ++i) {
+            const int d = 32 * i + 8 * g;
+            qf[i] = (rv && d < D) ? *reinterpret_cast<const u32x4_t*>(qrow + d * 2) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+    // zero V pad columns [D, DV) once (they feed the last O^T block)
+    if constexpr (C::DV > D) {
+        for (int idx = tid; idx < KS * (C::DV - D); idx += C::NT)
+            Vs[(idx / (C::DV - D)) * C::VP + D + idx % (C::DV - D)] = 0;
+    }
+    const int64_t mrow = HAS_MT ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)qi * p.ms[2] : 0;
+    const float c_scale = p.scale_log2;
+
+    float m_run = NEG_INF, l_run = 0.f;
+    f32x4_t oacc[C::NDBW];
+#pragma unroll
+    for (int i = 0; i < C::NDBW; ++i) oacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = kbeg; k0 < kend; k0 += KS) {
+        const int kw = k0 + 16 * w;  // this wave's first key
+        // ---- 1. issue every load of the chunk ----
+        u32x4_t kf[C::NCH];
+#pragma unroll
+        for (int i = 0; i < C::NCH; ++i) {
+            const int d = 32 * i + 8 * g;
+            kf[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (d < D) kf[i] = buffer_load16(krs, (uint32_t)(kw + col) * kstep32 + (uint32_t)(d * 2));
+        }
+        u32x4_t vr[C::VU];
+#pragma unroll
+        for (int u = 0; u < C::VU; ++u) {
+            const int idx = lane + 64 * u;
+            vr[u] = u32x4_t{0u, 0u, 0u, 0u};
+            if (idx < 16 * C::CPR)
+                vr[u] = buffer_load16(vrs, (uint32_t)(kw + idx / C::CPR) * vstep32 + (uint32_t)((idx % C::CPR) * 16));
+        }
+        typename MaskRaw<MASK>::type mr{};
+        if constexpr (HAS_MT) mr = load_mask_group<MASK>(p, mrow, kw + 4 * g);
+
+        // ---- 2. S^T = K Q^T (lane: row col, keys kw + 4 g + e) ----
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < C::NCH; ++i) s = Mma16<TR>::mma(kf[i], qf[i], s);
+
+        // ---- 3. chunk statistics ----
+        float x[4];
+        float mx = NEG_INF;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = kw + 4 * g + e;
+            float t = s[e] * c_scale;
+            bool ok = j < kend;
+            if constexpr (MASK == MASK_ADD16 || MASK == MASK_ADD32)
+                t = __builtin_fmaf(mask_value<MASK>(mr, e, p.mask_dtype), kLog2e, t);
+            if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
+            if constexpr (MASK == MASK_BOOL) ok = ok && ((mr >> (8 * e)) & 0xffu) != 0u;
+            x[e] = ok ? t : NEG_INF;
+            mx = fmaxf(mx, x[e]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (g == 0) red[0][w][col] = mx;
+        // V rows -> LDS (row-major, pitch VP; rows are 8-byte aligned, so two 8-byte stores)
+#pragma unroll
+        for (int u = 0; u < C::VU; ++u) {
+            const int idx = lane + 64 * u;
+            if (idx < 16 * C::CPR) {
+                uint16_t* dst = &Vs[(16 * w + idx / C::CPR) * C::VP + (idx % C::CPR) * 8];
+                reinterpret_cast<u32x2_t*>(dst)[0] = u32x2_t{vr[u][0], vr[u][1]};
+                reinterpret_cast<u32x2_t*>(dst)[1] = u32x2_t{vr[u][2], vr[u][3]};
+            }
+        }
+        __syncthreads();
+        float mc = NEG_INF;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) mc = fmaxf(mc, red[0][i][col]);
+        const float m_new = fmaxf(m_run, mc);
+        const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
+        const float muse = (m_new == NEG_INF) ? 0.f : m_new;
+        m_run = m_new;
+        float ls = 0.f;
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pe[e] = fast_exp2(x[e] - muse);
+            ls += pe[e];
+        }
+        ls += __shfl_xor(ls, 16, 64);
+        ls += __shfl_xor(ls, 32, 64);
+        if (g == 0) red[1][w][col] = ls;
+        *reinterpret_cast<u32x2_t*>(&Ps[col * C::PP + 16 * w + 4 * g]) =
+            u32x2_t{TR::pack(pe[0], pe[1]), TR::pack(pe[2], pe[3])};
+        __syncthreads();
+        float lc = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) lc += red[1][i][col];
+        l_run = l_run * alpha + lc;
+
+        // ---- 4. O^T += V^T P^T over the chunk, this wave's head-dim blocks ----
+#pragma unroll
+        for (int i = 0; i < C::NDBW; ++i) {
+            const int db = w + NW * i;
+            if (db >= C::NDB) break;
+            f32x4_t acc = oacc[i] * alpha;
+#pragma unroll
+            for (int ks = 0; ks < KS / 32; ++ks) {
+                const u32x4_t bf = *reinterpret_cast<const u32x4_t*>(&Ps[col * C::PP + 32 * ks + 8 * g]);
+                const uint16_t* vp = &Vs[(32 * ks + 8 * g) * C::VP + 16 * db + col];
+                u32x4_t af;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    af[e] = (uint32_t)vp[(2 * e) * C::VP] | ((uint32_t)vp[(2 * e + 1) * C::VP] << 16);
+                acc = Mma16<TR>::mma(af, bf, acc);
+            }
+            oacc[i] = acc;
+        }
+        __syncthreads();  // Vs / Ps / red are rewritten by the next chunk
+    }
+
+    // ---- partial state of this split ----
+    if (rv) {
+        const int64_t row = ((int64_t)b * p.Hq + qh) * p.Lq + qi;
+        float* po = p.ws_o + (row * p.splits + split) * D;
+#pragma unroll
+        for (int i = 0; i < C::NDBW; ++i) {
+            const int db = w + NW * i;
+            if (db >= C::NDB) break;
+            const int d = 16 * db + 4 * g;
+            if (d < D) *reinterpret_cast<f32x4_t*>(po + d) = oacc[i];
+        }
+        if (w == 0 && g == 0) {
+            p.ws_ml[(row * p.splits + split) * 2 + 0] = m_run;
+            p.ws_ml[(row * p.splits + split) * 2 + 1] = l_run;
+        }
+    }
+}
+
+}  // namespace sdpa_dev

@@ -13,7 +13,8 @@ using sdpa_dev::Params;
 typedef hipError_t (*launch_fn)(const Params&, dim3 grid, hipStream_t stream);
 
 struct TileInfo {
-    int bn;   // keys per tile
+    int bn;   // keys per tile (decode: keys per chunk; a split is a whole number of chunks)
+    int cols; // query columns per workgroup (prefill: query rows; decode: query-head x row pairs)
     int wm;   // 32-column blocks per workgroup
     int wd;   // waves splitting the head dim
     int nt;   // threads per workgroup

@@ -110,7 +110,7 @@ struct DecodePlan {
 DecodePlan decode_plan(int batch, int q_len, int kv_len, int hq, int hkv, const sdpa_host::TileInfo& t) {
     DecodePlan p;
     const int rows = (hq / hkv) * q_len;
-    const int cols = 32 * t.wm;
+    const int cols = t.cols;
     p.col_groups = (rows + cols - 1) / cols;
     const long groups = (long)batch * hkv * p.col_groups;
     const int max_splits = (kv_len + t.bn - 1) / t.bn;
@@ -194,16 +194,16 @@ std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int 
         const auto& t = ks->full_cfg;
         std::snprintf(buf, sizeof buf,
                       "full %s d%d %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d tile=%dx%d waves=%dx%d lds=%d",
-                      dtype_name(dt), d, mask_name(mk), batch, q_len, kv_len, hq, hkv, 32 * t.wm, t.bn, t.wm, t.wd,
+                      dtype_name(dt), d, mask_name(mk), batch, q_len, kv_len, hq, hkv, t.cols, t.bn, t.wm, t.wd,
                       t.lds);
     } else {
         const auto& t = ks->dec_cfg;
         DecodePlan p = decode_plan(batch, q_len, kv_len, hq, hkv, t);
         std::snprintf(buf, sizeof buf,
                       "vector %s d%d %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d splits=%d keys/split=%d colgroups=%d "
-                      "waves=%dx%d lds=%d",
+                      "cols=%d threads=%d lds=%d",
                       dtype_name(dt), d, mask_name(mk), batch, q_len, kv_len, hq, hkv, p.splits, p.keys_per_split,
-                      p.col_groups, t.wm, t.wd, t.lds);
+                      p.col_groups, t.cols, t.nt, t.lds);
     }
     return buf;
 }
@@ -432,7 +432,7 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
 
     if (kern == SDPA_KERNEL_FULL) {
         const auto& t = ks->full_cfg;
-        const int bm = 32 * t.wm;
+        const int bm = t.cols;
         // one-dimensional grid: 8 XCDs x ceil(items / 8), items = (batch, head, query tile)
         const long items = (long)((q_len + bm - 1) / bm) * n_q_heads * batch;
         if (items > (1L << 30)) return reject(SDPA_EUNSUPPORTED);
