@@ -48,12 +48,13 @@ def _run(cmd):
     return time.time() - t, err
 
 
-def build(jobs: int | None = None, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = True, defines=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every unit and link `out`; `defines` are extra -D flags (tuning experiments)."""
+    os.makedirs(build_dir, exist_ok=True)
     tmpl = open(os.path.join(CSRC, "inst_template.hip.in")).read()
     units = []
     for d in head_dims():
-        path = os.path.join(BUILD, f"inst_d{d}.hip")
+        path = os.path.join(build_dir, f"inst_d{d}.hip")
         text = tmpl.replace("@D@", str(d))
         if not os.path.exists(path) or open(path).read() != text:
             with open(path, "w") as f:
@@ -63,10 +64,10 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     objs = []
     cmds = []
     for u in units:
-        o = os.path.join(BUILD, os.path.basename(u) + ".o")
+        o = os.path.join(build_dir, os.path.basename(u) + ".o")
         objs.append(o)
         lang = ["-x", "hip"] if u.endswith(".cpp") else []
-        cmds.append([HIPCC] + COMMON + lang + ["-c", u, "-o", o])
+        cmds.append([HIPCC] + COMMON + [f"-D{x}" for x in defines] + lang + ["-c", u, "-o", o])
     jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
     t0 = time.time()
     with cf.ThreadPoolExecutor(jobs) as ex:
@@ -75,16 +76,19 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
                 print(f"[build] {os.path.basename(cmd[-3])}: {dt:.1f}s", flush=True)
             if err.strip() and verbose:
                 print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"[build] {LIB} ({time.time() - t0:.1f}s)", flush=True)
-    return LIB
+        print(f"[build] {out} ({time.time() - t0:.1f}s)", flush=True)
+    return out
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra preprocessor define")
+    ap.add_argument("--out", default=LIB)
+    ap.add_argument("--build-dir", default=BUILD)
     a = ap.parse_args()
-    build(a.jobs)
+    build(a.jobs, defines=a.defines, out=os.path.abspath(a.out), build_dir=os.path.abspath(a.build_dir))

@@ -449,54 +449,98 @@ __global__ __launch_bounds__(C::NT, C::OCC) void attn_tile_kernel(const Params p
     }
 }
 
-// Decode combine: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s over the
-// splits in ascending order (deterministic).  One wave per (output row,
-// 64-wide slice of d): grid = (B*Hq*Lq, ceil(D/64)).  The wave first turns the
-// split maxima into weights in LDS, then each lane accumulates one d.
+// Decode combine: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+// One workgroup (4 waves) per (output row, 64-wide slice of d): lane l of
+// wave w reads float4 column group l % 16 of splits s = 4 * (16 * i + w) +
+// l / 16 ... so every partial load of the workgroup is in flight at once;
+// the four split phases of a wave and the four waves are then summed in a
+// fixed order (deterministic).  grid = (B*Hq*Lq, ceil(D/64)).
 constexpr int kMaxSplits = 1024;
 
 template <class TR, int D>
-__global__ __launch_bounds__(64) void combine_kernel(const Params p) {
+__global__ __launch_bounds__(256) void combine_kernel(const Params p) {
     constexpr float NEG_INF = -__builtin_inff();
+    constexpr int MAXI = 4;  // splits per lane held in registers per pass
     __shared__ float wts[kMaxSplits];
+    __shared__ float redm[4], redl[4];
+    __shared__ f32x4_t part[4][16];
     const int64_t row = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int S = p.splits;
+    const int cgp = lane & 15, ph = lane >> 4;   // float4 column group, split phase
+    const int d = blockIdx.y * 64 + 4 * cgp;
+    const bool dv = d < D;
+    const float* po = p.ws_o + row * S * D + d;
     const float* ml = p.ws_ml + row * S * 2;
+    // first pass of partial loads is issued before anything depends on it
+    f32x4_t v[MAXI];
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        const int s = 16 * i + 4 * w + ph;
+        v[i] = (dv && s < S) ? *reinterpret_cast<const f32x4_t*>(po + (int64_t)s * D) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    float mreg[kMaxSplits / 256], lreg[kMaxSplits / 256];
     float M = NEG_INF;
-    for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+    for (int i = 0; i < kMaxSplits / 256; ++i) {
+        const int s = tid + 256 * i;
+        mreg[i] = s < S ? ml[2 * s] : NEG_INF;
+        lreg[i] = s < S ? ml[2 * s + 1] : 0.f;
+        M = fmaxf(M, mreg[i]);
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    if (lane == 0) redm[w] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
     float den = 0.f;
-    for (int s = lane; s < S; s += 64) {
-        const float ms = ml[2 * s];
-        const float w = (ms == NEG_INF) ? 0.f : fast_exp2(ms - M);
-        wts[s] = w;
-        den = __builtin_fmaf(w, ml[2 * s + 1], den);
+#pragma unroll
+    for (int i = 0; i < kMaxSplits / 256; ++i) {
+        const int s = tid + 256 * i;
+        const float wv = (mreg[i] == NEG_INF || M == NEG_INF) ? 0.f : fast_exp2(mreg[i] - M);
+        if (s < S) wts[s] = wv;
+        den = __builtin_fmaf(wv, lreg[i], den);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
+    if (lane == 0) redl[w] = den;
     __syncthreads();
-    const int d = blockIdx.y * 64 + lane;
-    if (d >= D) return;
-    const float* po = p.ws_o + row * S * D + d;
-    float num = 0.f;
-    int s = 0;
-    for (; s + 8 <= S; s += 8) {
-        float v[8];
+    den = (redl[0] + redl[1]) + (redl[2] + redl[3]);
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += 16 * MAXI) {
+        if (s0 > 0) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = po[(int64_t)(s + k) * D];
+            for (int i = 0; i < MAXI; ++i) {
+                const int s = s0 + 16 * i + 4 * w + ph;
+                v[i] = (dv && s < S) ? *reinterpret_cast<const f32x4_t*>(po + (int64_t)s * D)
+                                     : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) num = __builtin_fmaf(wts[s + k], v[k], num);
+        for (int i = 0; i < MAXI; ++i) {
+            const int s = s0 + 16 * i + 4 * w + ph;
+            const float wv = s < S ? wts[s] : 0.f;
+            acc += wv * v[i];
+        }
     }
-    for (; s < S; ++s) num = __builtin_fmaf(wts[s], po[(int64_t)s * D], num);
-    const float val = (M != NEG_INF && den > 0.f) ? num / den : 0.f;
+    // sum the 4 split phases of the wave (lanes 16 apart), then the 4 waves
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        acc[k] += __shfl_xor(acc[k], 16, 64);
+        acc[k] += __shfl_xor(acc[k], 32, 64);
+    }
+    if (ph == 0) part[w][cgp] = acc;
+    __syncthreads();
+    if (w != 0 || ph != 0 || !dv) return;
+    const f32x4_t tot = (part[0][cgp] + part[1][cgp]) + (part[2][cgp] + part[3][cgp]);
+    const float inv = (M != NEG_INF && den > 0.f) ? 1.f / den : 0.f;
     const int qi = (int)(row % p.Lq);
     const int64_t bh = row / p.Lq;
     const int qh = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
     char* dst = reinterpret_cast<char*>(p.o) +
                 ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2] + d) * TR::ES;
-    TR::store1(dst, val);
+    TR::store4(dst, tot * inv);
 }
 
 }  // namespace sdpa_dev

@@ -15,8 +15,9 @@
 //      over lanes (shuffles) and over waves (LDS); the chunk is merged into
 //      the running state with the usual 2^(m_old - m_new) rescale;
 //   4. P (rounded to the input type) goes to LDS; O^T += V^T P^T on the matrix
-//      cores, each wave owning every NW-th 16-column block of the head dim
-//      and reading V^T columns out of the row-major LDS copy.
+//      cores, each wave owning every NW-th 16-column block of the head dim.
+//      V is stored transposed in LDS ([d][key], 4-key x 8-column register
+//      transposes on the way in), so each A operand is one 16-byte read.
 // The workgroup writes its unnormalised partial output, running max (log2
 // domain) and sum; combine_kernel merges the splits.
 #pragma once
@@ -45,11 +46,12 @@ struct DecCfg {
     static constexpr int DV = (D + 15) / 16 * 16;    // V columns incl. zero pad
     static constexpr int NDB = DV / 16;              // 16-column O^T blocks
     static constexpr int NDBW = (NDB + NW - 1) / NW; // blocks per wave (round robin)
-    static constexpr int VP = DV + 4;                // V row pitch (elements): rows 8 apart land 64 B apart
+    static constexpr int TP = KS + 4;                // V^T row pitch: 8-byte rows skew, so the 8 rows a
+                                                     // transposed store hits at once fall on distinct banks
     static constexpr int PP = KS + 8;                // P row pitch (elements)
     static constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
-    static constexpr int VU = (16 * CPR + 63) / 64;  // V chunks per lane
-    static constexpr int LDS = KS * VP * 2 + 16 * PP * 2 + 2 * NW * 16 * 4;
+    static constexpr int VU = (4 * CPR + 63) / 64;   // (4-key, 8-column) V units per lane
+    static constexpr int LDS = DV * TP * 2 + 16 * PP * 2 + 2 * NW * 16 * 4;
     static_assert(D % 8 == 0, "head dim must be a whole number of 16-byte chunks");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
     constexpr int D = C::D, NW = C::NW, KS = C::KS;
     constexpr float NEG_INF = -__builtin_inff();
     constexpr bool HAS_MT = (MASK == MASK_ADD16 || MASK == MASK_ADD32 || MASK == MASK_BOOL);
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[KS * C::VP];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[C::DV * C::TP];
     __shared__ __attribute__((aligned(16))) uint16_t Ps[16 * C::PP];
     __shared__ float red[2][NW][16];
 
@@ -95,10 +97,9 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
             qf[i] = (rv && d < D) ? *reinterpret_cast<const u32x4_t*>(qrow + d * 2) : u32x4_t{0u, 0u, 0u, 0u};
         }
     }
-    // zero V pad columns [D, DV) once (they feed the last O^T block)
+    // zero V^T pad rows [D, DV) once (they feed the last O^T block)
     if constexpr (C::DV > D) {
-        for (int idx = tid; idx < KS * (C::DV - D); idx += C::NT)
-            Vs[(idx / (C::DV - D)) * C::VP + D + idx % (C::DV - D)] = 0;
+        for (int idx = tid; idx < (C::DV - D) * C::TP; idx += C::NT) Vt[D * C::TP + idx] = 0;
     }
     const int64_t mrow = HAS_MT ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)qi * p.ms[2] : 0;
     const float c_scale = p.scale_log2;
@@ -118,13 +119,20 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
             kf[i] = u32x4_t{0u, 0u, 0u, 0u};
             if (d < D) kf[i] = buffer_load16(krs, (uint32_t)(kw + col) * kstep32 + (uint32_t)(d * 2));
         }
-        u32x4_t vr[C::VU];
+        // V unit u of this lane: keys kw + 4 * q4 .. +3, head-dim columns 8 c .. +7
+        // (the key quad varies fastest across lanes, so the transposed LDS stores
+        // of one instruction spread over 16 column groups x 4 quads of banks)
+        u32x4_t vr[C::VU][4];
 #pragma unroll
         for (int u = 0; u < C::VU; ++u) {
             const int idx = lane + 64 * u;
-            vr[u] = u32x4_t{0u, 0u, 0u, 0u};
-            if (idx < 16 * C::CPR)
-                vr[u] = buffer_load16(vrs, (uint32_t)(kw + idx / C::CPR) * vstep32 + (uint32_t)((idx % C::CPR) * 16));
+            const int q4 = idx & 3, c = idx >> 2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vr[u][e] = u32x4_t{0u, 0u, 0u, 0u};
+                if (idx < 4 * C::CPR)
+                    vr[u][e] = buffer_load16(vrs, (uint32_t)(kw + 4 * q4 + e) * vstep32 + (uint32_t)(c * 16));
+            }
         }
         typename MaskRaw<MASK>::type mr{};
         if constexpr (HAS_MT) mr = load_mask_group<MASK>(p, mrow, kw + 4 * g);
@@ -152,14 +160,23 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         if (g == 0) red[0][w][col] = mx;
-        // V rows -> LDS (row-major, pitch VP; rows are 8-byte aligned, so two 8-byte stores)
+        // V -> LDS transposed: 4 keys x 8 columns -> 8 rows of V^T, 4 keys (8 bytes) each
 #pragma unroll
         for (int u = 0; u < C::VU; ++u) {
             const int idx = lane + 64 * u;
-            if (idx < 16 * C::CPR) {
-                uint16_t* dst = &Vs[(16 * w + idx / C::CPR) * C::VP + (idx % C::CPR) * 8];
-                reinterpret_cast<u32x2_t*>(dst)[0] = u32x2_t{vr[u][0], vr[u][1]};
-                reinterpret_cast<u32x2_t*>(dst)[1] = u32x2_t{vr[u][2], vr[u][3]};
+            if (idx < 4 * C::CPR) {
+                const int q4 = idx & 3, c = idx >> 2;
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+                        const uint32_t lo = __builtin_amdgcn_perm(vr[u][1][wd], vr[u][0][wd], sel);
+                        const uint32_t hi = __builtin_amdgcn_perm(vr[u][3][wd], vr[u][2][wd], sel);
+                        *reinterpret_cast<u32x2_t*>(&Vt[(8 * c + 2 * wd + e) * C::TP + 16 * w + 4 * q4]) =
+                            u32x2_t{lo, hi};
+                    }
+                }
             }
         }
         __syncthreads();
@@ -197,16 +214,15 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
 #pragma unroll
             for (int ks = 0; ks < KS / 32; ++ks) {
                 const u32x4_t bf = *reinterpret_cast<const u32x4_t*>(&Ps[col * C::PP + 32 * ks + 8 * g]);
-                const uint16_t* vp = &Vs[(32 * ks + 8 * g) * C::VP + 16 * db + col];
-                u32x4_t af;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    af[e] = (uint32_t)vp[(2 * e) * C::VP] | ((uint32_t)vp[(2 * e + 1) * C::VP] << 16);
+                const uint16_t* vt = &Vt[(16 * db + col) * C::TP + 32 * ks + 8 * g];
+                const u32x2_t a0 = reinterpret_cast<const u32x2_t*>(vt)[0];
+                const u32x2_t a1 = reinterpret_cast<const u32x2_t*>(vt)[1];
+                const u32x4_t af = {a0[0], a0[1], a1[0], a1[1]};
                 acc = Mma16<TR>::mma(af, bf, acc);
             }
             oacc[i] = acc;
         }
-        __syncthreads();  // Vs / Ps / red are rewritten by the next chunk
+        __syncthreads();  // Vt / Ps / red are rewritten by the next chunk
     }
 
     // ---- partial state of this split ----
