@@ -78,6 +78,14 @@ def build(jobs: int | None = None, verbose: bool = True, defines=(), out: str = 
                 print(err, file=sys.stderr)
     tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
+    # a kernel whose host stub was not emitted shows up as an undefined symbol
+    nm = shutil.which("nm")
+    if nm:
+        und = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+        bad = [l.split()[-1] for l in und.splitlines() if "sdpa_dev" in l or "sdpa_host" in l]
+        if bad:
+            os.remove(tmp)
+            raise RuntimeError(f"build failed: {len(bad)} undefined library symbols, e.g. {bad[0]}")
     os.replace(tmp, out)
     if verbose:
         print(f"[build] {out} ({time.time() - t0:.1f}s)", flush=True)

@@ -135,6 +135,27 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint3
     return bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// 16 bytes per lane, global -> LDS without passing through registers: lane l
+// writes at lds_base + 16 * l (buffer_load_dwordx4 ... lds).  The builtin
+// exists for the device target only; the host pass sees an empty body.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+#endif
+}
+
+// ds_read_b64_tr_b16: in each 16-lane group, output lane i element e is
+// element i % 4 of the 4 values at the address of source lane 4 e + i / 4.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef short v4i16_t __attribute__((ext_vector_type(4)));
+    return bitcast<u32x2_t>(__builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16_t*)(const_cast<void*>(addr))));
+#else
+    return u32x2_t{0u, 0u};
+#endif
+}
+
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // ---------------------------------------------------------------------------

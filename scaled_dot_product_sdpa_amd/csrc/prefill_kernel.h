@@ -1,0 +1,299 @@
+// Prefill ("full") kernel for 16-bit inputs and head dims up to 128 on gfx950.
+//
+// Same mathematics and work split as attn_tile_kernel (S^T = K Q^T and
+// O^T = V^T P^T on v_mfma_f32_32x32x16, 32 query columns per wave, online
+// softmax in base 2, XCD-aware longest-first grid), with the data path
+// rebuilt around two gfx950 features:
+//   * K and V tiles move global -> LDS with buffer_load_dwordx4 ... lds: each
+//     lane of a load writes its 16 bytes at LDS base + 16 * lane, so a tile is
+//     stored row-major with rows of KC + 1 sixteen-byte chunks (KC = D / 8).
+//     The extra chunk is never loaded: it staggers rows over the LDS banks
+//     and holds constants (zeros for K; for V, a one at column D when D is
+//     not a multiple of 32, so the P V product also yields the softmax row
+//     sums).  Two stages are double-buffered: the loads of tile t + 1 fly
+//     while tile t is computed, with one barrier per tile.
+//   * The A operand of P V (V^T: one head-dim column, eight keys per lane)
+//     comes straight from the row-major V tile through ds_read_b64_tr_b16:
+//     in each 16-lane group, source lane 4 e + j names the 4 columns
+//     4 j .. 4 j + 3 of key e, and output lane i receives column i of keys
+//     0..3; two reads give the eight keys a lane's P registers hold.
+// Tiles with no per-element mask (full, unmasked, left of the causal
+// diagonal) run a separate loop from masked ones, so neither pays for the
+// other's code.
+#pragma once
+
+#include "attn_common.h"
+
+namespace sdpa_dev {
+
+template <class TR, int D_, int BN_, int WM_, int OCC_>
+struct PfCfg {
+    static constexpr int D = D_, BN = BN_, WM = WM_, OCC = OCC_;
+    static constexpr int NT = 64 * WM, BM = 32 * WM;
+    static constexpr int KC = D / 8;                  // 16-byte chunks per row
+    static constexpr int RC = KC + 1;                 // chunks per LDS row (one spare)
+    static constexpr int ROWB = RC * 16;              // bytes per LDS row
+    static constexpr int TILEB = BN * ROWB;           // bytes per K or V tile
+    static constexpr int NCH = (D + 15) / 16;         // Q K^T chunks (16 head-dim columns)
+    static constexpr int NDB = (D + 31) / 32;         // 32-column O^T blocks
+    static constexpr int NKB = BN / 32;               // 32-key score blocks per tile
+    static constexpr bool ONES = (D % 32) != 0;
+    static constexpr int SLOTS = BN * RC;             // 16-byte slots per tile
+    static constexpr int NLD = (SLOTS + NT - 1) / NT; // load instructions per thread per tile (K or V)
+    static constexpr int LDS = 4 * TILEB + 64;        // K0, V0, K1, V1 (+ slack read past the last row)
+    static_assert(D % 8 == 0 && D <= 128, "head dim");
+    static_assert(BN % 32 == 0, "key tile");
+    static_assert(!ONES || (D % 32) <= 16, "ones column must sit in the spare chunk");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <class TR, class C, int MASK>
+__global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) {
+    constexpr int D = C::D, BN = C::BN, BM = C::BM;
+    constexpr float NEG_INF = -__builtin_inff();
+    constexpr float kRescale = 8.0f;
+    constexpr bool HAS_MT = (MASK == MASK_ADD16 || MASK == MASK_ADD32 || MASK == MASK_BOOL);
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wm = tid >> 6;
+    const int col = lane & 31, hh = lane >> 5;
+
+    // ---- work item (XCD-aware, longest causal tiles first) ----
+    const int nqt = (p.Lq + BM - 1) / BM;
+    const int total = nqt * p.Hq * p.B;
+    const int per = (total + 7) / 8;
+    const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (item >= total) return;
+    const int tt = item % nqt, bh = item / nqt;
+    const int qh = bh % p.Hq, b = bh / p.Hq;
+    const int t = (MASK == MASK_CAUSAL) ? nqt - 1 - tt : tt;
+    const int g = qh / p.n_rep;
+    const int i0 = t * BM;
+    const int qmin = i0 + 32 * wm;  // first query row of this wave
+    const int qi = qmin + col;
+    const bool rv = qi < p.Lq;
+    const int off = p.Lk - p.Lq;
+    int kend = p.Lk;
+    if (MASK == MASK_CAUSAL) {
+        const int64_t e = (int64_t)i0 + BM + off;
+        kend = (int)(e < 0 ? 0 : (e > p.Lk ? p.Lk : e));
+    }
+    // keys [0, kplain) need no per-element mask for any row of this wave
+    int kplain = kend;
+    if (MASK == MASK_CAUSAL) kplain = min(kend, max(0, qmin + off + 1));
+    if (HAS_MT || !p.scale_nonneg) kplain = 0;
+    kplain = (kplain / BN) * BN;  // whole tiles only
+    const int ntiles = (kend + BN - 1) / BN;
+
+    // ---- buffer resources over this (batch, kv head)'s K and V rows ----
+    const int64_t kstep = (int64_t)p.ks[2] * 2, vstep = (int64_t)p.vs[2] * 2;
+    const char* kglob = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)g * p.ks[1]) * 2;
+    const char* vglob = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)g * p.vs[1]) * 2;
+    const uint32_t kstep32 = (uint32_t)kstep, vstep32 = (uint32_t)vstep;
+    const __amdgpu_buffer_rsrc_t krs =
+        make_rsrc(kglob, kend > 0 ? (uint32_t)(kend - 1) * kstep32 + (uint32_t)(D * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t vrs =
+        make_rsrc(vglob, kend > 0 ? (uint32_t)(kend - 1) * vstep32 + (uint32_t)(D * 2) : 0u);
+
+    // ---- Q fragments (MFMA B operand), zero beyond D / beyond the rows ----
+    u32x4_t qf[C::NCH];
+    {
+        const char* qrow = reinterpret_cast<const char*>(p.q) +
+                           ((int64_t)b * p.qs[0] + (int64_t)qh * p.qs[1] + (int64_t)qi * p.qs[2]) * 2;
+#pragma unroll
+        for (int ch = 0; ch < C::NCH; ++ch) {
+            const int d = ch * 16 + hh * 8;
+            qf[ch] = (rv && d < D) ? *reinterpret_cast<const u32x4_t*>(qrow + d * 2) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+
+    // ---- spare chunks: K rows 0, V rows (1 at column D if ONES, else 0) ----
+    for (int r = tid; r < 4 * BN; r += C::NT) {
+        const int tile = r / BN, row = r % BN;  // tiles K0, V0, K1, V1
+        const bool is_v = tile & 1;
+        u32x4_t z = {0u, 0u, 0u, 0u};
+        if (is_v && C::ONES) z[0] = OneBits<TR>::v;
+        *reinterpret_cast<u32x4_t*>(smem + tile * C::TILEB + row * C::ROWB + C::KC * 16) = z;
+    }
+
+    // ---- load slots: lane slot s -> (row, chunk); the spare chunk is never loaded ----
+    uint32_t kofs[C::NLD], vofs[C::NLD];
+    bool sok[C::NLD];
+#pragma unroll
+    for (int u = 0; u < C::NLD; ++u) {
+        const int s = (u * C::WM + wm) * 64 + lane;  // this lane's 16-byte slot of the tile
+        const int row = s / C::RC, ch = s % C::RC;
+        sok[u] = (s < C::SLOTS) && (ch < C::KC);
+        kofs[u] = (uint32_t)row * kstep32 + (uint32_t)(ch * 16);
+        vofs[u] = (uint32_t)row * vstep32 + (uint32_t)(ch * 16);
+    }
+    auto issue_tile = [&](int kt, int stage) {
+        char* kt_lds = smem + (2 * stage) * C::TILEB;
+        char* vt_lds = smem + (2 * stage + 1) * C::TILEB;
+        const uint32_t kb0 = (uint32_t)kt * kstep32, vb0 = (uint32_t)kt * vstep32;
+#pragma unroll
+        for (int u = 0; u < C::NLD; ++u) {
+            const int blk = (u * C::WM + wm) * 64 * 16;  // LDS byte offset of this instruction's 64 slots
+            if (blk >= C::SLOTS * 16) break;
+            if (sok[u]) {
+                buffer_load16_lds(krs, kt_lds + blk, kofs[u] + kb0);
+                buffer_load16_lds(vrs, vt_lds + blk, vofs[u] + vb0);
+            }
+        }
+    };
+
+    const int64_t mrow = HAS_MT ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)(rv ? qi : 0) * p.ms[2] : 0;
+    typename MaskRaw<MASK>::type mr[HAS_MT ? C::NKB : 1][4];
+    auto load_mask = [&](int kt) {
+        if constexpr (HAS_MT) {
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) mr[kb][a4] = load_mask_group<MASK>(p, mrow, kt + kb * 32 + 8 * a4 + 4 * hh);
+        }
+    };
+
+    float m_run = NEG_INF, l_run = 0.f;
+    f32x16_t oacc[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16_t{};
+    const float c_scale = p.scale_log2;
+
+    // S^T of one tile from LDS stage `stage`
+    auto scores = [&](int stage, f32x16_t (&sacc)[C::NKB]) {
+        const char* kt_lds = smem + (2 * stage) * C::TILEB;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+            sacc[kb] = f32x16_t{};
+#pragma unroll
+            for (int ch = 0; ch < C::NCH; ++ch) {
+                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+                    kt_lds + (kb * 32 + col) * C::ROWB + (2 * ch + hh) * 16);
+                sacc[kb] = TR::mma(a, qf[ch], sacc[kb]);
+            }
+        }
+    };
+    // online softmax on scores already scaled (c_eff = 1) or raw (c_eff = scale)
+    auto softmax_pv = [&](int stage, f32x16_t (&sacc)[C::NKB], float mtile, float c_eff) {
+        mtile = fmaxf(mtile, xor32(mtile));
+        if (__any(mtile > m_run + kRescale)) {
+            const float m_new = fmaxf(m_run, mtile);
+            const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        const float muse = (m_run == NEG_INF) ? 0.f : m_run;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = fast_exp2(__builtin_fmaf(sacc[kb][r], c_eff, -muse));
+                sacc[kb][r] = e;
+                lsum += e;
+            }
+        if constexpr (!C::ONES) l_run += lsum;
+        // O^T += V^T P^T; V^T operands via transposed LDS reads of the row-major V tile
+        const char* vt_lds = smem + (2 * stage + 1) * C::TILEB;
+        const int grp = lane >> 4, s16 = lane & 15;
+        const int e4 = s16 >> 2, j4 = s16 & 3;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc) {
+                u32x4_t bf;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) bf[w] = TR::pack(sacc[kb][8 * pc + 2 * w], sacc[kb][8 * pc + 2 * w + 1]);
+                const int key = kb * 32 + 16 * pc + 4 * (grp >> 1) + e4;
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db) {
+                    const int d = 32 * db + 16 * (grp & 1) + 4 * j4;
+                    const char* a0 = vt_lds + key * C::ROWB + d * 2;
+                    const u32x2_t y0 = lds_read_tr16(a0);
+                    const u32x2_t y1 = lds_read_tr16(a0 + 8 * C::ROWB);
+                    oacc[db] = TR::mma(u32x4_t{y0[0], y0[1], y1[0], y1[1]}, bf, oacc[db]);
+                }
+            }
+        }
+    };
+
+    if (ntiles > 0) {
+        issue_tile(0, 0);
+        load_mask(0);
+    }
+    for (int it = 0; it < ntiles; ++it) {
+        const int kt = it * BN, stage = it & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // tile `it` is in LDS; every wave is done with the other stage
+        if (it + 1 < ntiles) issue_tile(kt + BN, stage ^ 1);
+        f32x16_t sacc[C::NKB];
+        scores(stage, sacc);
+        if (kt + BN <= kplain) {
+            // no per-element mask: row max on unscaled scores
+            float mx = NEG_INF;
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+            if (it + 1 < ntiles) load_mask(kt + BN);
+            softmax_pv(stage, sacc, mx * c_scale, c_scale);
+        } else {
+            float mtile = NEG_INF;
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = kt + kb * 32 + 8 * a4 + 4 * hh + r;
+                        float x = sacc[kb][4 * a4 + r] * c_scale;
+                        bool ok = j < kend;
+                        if constexpr (MASK == MASK_ADD16 || MASK == MASK_ADD32)
+                            x = __builtin_fmaf(mask_value<MASK>(mr[kb][a4], r, p.mask_dtype), kLog2e, x);
+                        if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
+                        if constexpr (MASK == MASK_BOOL) ok = ok && ((mr[kb][a4] >> (8 * r)) & 0xffu) != 0u;
+                        x = ok ? x : NEG_INF;
+                        sacc[kb][4 * a4 + r] = x;
+                        mtile = fmaxf(mtile, x);
+                    }
+                }
+            }
+            if (it + 1 < ntiles) load_mask(kt + BN);
+            softmax_pv(stage, sacc, mtile, 1.f);
+        }
+    }
+
+    // ---- epilogue ----
+    float lsum_row;
+    if constexpr (C::ONES) {
+        constexpr int rr = D % 32;
+        constexpr int RL = 4 * (rr / 8) + (rr % 4), HL = (rr % 8) / 4, DBL = D / 32;
+        const float x = oacc[DBL][RL];
+        const float y = xor32(x);
+        lsum_row = (hh == HL) ? x : y;
+    } else {
+        lsum_row = l_run + xor32(l_run);
+    }
+    if (rv) {
+        const float inv = lsum_row > 0.f ? 1.f / lsum_row : 0.f;
+        char* orow = reinterpret_cast<char*>(p.o) +
+                     ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2]) * 2;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d0 = 32 * db + 8 * a4 + 4 * hh;
+                if (d0 < D) {
+                    f32x4_t x = {oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv, oacc[db][4 * a4 + 2] * inv,
+                                 oacc[db][4 * a4 + 3] * inv};
+                    TR::store4(orow + d0 * 2, x);
+                }
+            }
+    }
+}
+
+}  // namespace sdpa_dev
