@@ -64,14 +64,16 @@ __device__ __forceinline__ To bitcast(const From& x) {
     return __builtin_bit_cast(To, x);
 }
 
-// Round-to-nearest-even float -> bf16 / f16 pairs, packed low = a, high = b.
+// Round-to-nearest-even float -> bf16 / f16 pairs, packed low = a, high = b
+// (one v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 per pair).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)bitcast<uint16_t>(x) | ((uint32_t)bitcast<uint16_t>(y) << 16);
+    return bitcast<uint32_t>(__builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-    _Float16 x = (_Float16)a, y = (_Float16)b;
-    return (uint32_t)bitcast<uint16_t>(x) | ((uint32_t)bitcast<uint16_t>(y) << 16);
+    return bitcast<uint32_t>(__builtin_convertvector(f32x2_t{a, b}, f16x2_t));
 }
 
 // ---------------------------------------------------------------------------
