@@ -111,6 +111,19 @@ struct TF16 {
     }
 };
 
+// 16x16x32 MFMA (lane l: column l % 16, rows 4 * (l / 16) + i of the output)
+template <class TR> struct Mma16;
+template <> struct Mma16<TBF16> {
+    static __device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
+    }
+};
+template <> struct Mma16<TF16> {
+    static __device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
+    }
+};
+
 // float32 stays float32 end to end: v_mfma_f32_32x32x2_f32, no reduced-precision mode.
 struct TF32 {
     static constexpr int ES = 4, EPC = 4, KCH = 8, DT = MDT_F32;

@@ -26,18 +26,6 @@
 
 namespace sdpa_dev {
 
-template <class TR> struct Mma16;
-template <> struct Mma16<TBF16> {
-    static __device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
-    }
-};
-template <> struct Mma16<TF16> {
-    static __device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
-    }
-};
-
 template <class TR, int D_, int NW_>
 struct DecCfg {
     static constexpr int D = D_, NW = NW_, NT = 64 * NW;

@@ -19,6 +19,7 @@ struct TileInfo {
     int wd;   // waves splitting the head dim
     int nt;   // threads per workgroup
     int lds;  // bytes of LDS per workgroup
+    int heads = 1;  // prefill: query heads of one grouped-query group sharing a workgroup (at most)
 };
 
 struct KernelSet {

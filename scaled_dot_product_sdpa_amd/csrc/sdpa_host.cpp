@@ -432,9 +432,18 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
 
     if (kern == SDPA_KERNEL_FULL) {
         const auto& t = ks->full_cfg;
-        const int bm = t.cols;
-        // one-dimensional grid: 8 XCDs x ceil(items / 8), items = (batch, head, query tile)
-        const long items = (long)((q_len + bm - 1) / bm) * n_q_heads * batch;
+        // heads of one group that share a workgroup: the largest power of two up
+        // to t.heads dividing the group size (the kernel derives the same number)
+        const int rep = n_q_heads / n_kv_heads;
+        int hg = 1;
+        for (int c = t.heads; c > 1; c >>= 1)
+            if (rep % c == 0) {
+                hg = c;
+                break;
+            }
+        const int bm = t.cols / hg;
+        // one-dimensional grid: 8 XCDs x ceil(items / 8), items = (batch, head group, query tile)
+        const long items = (long)((q_len + bm - 1) / bm) * (n_q_heads / hg) * batch;
         if (items > (1L << 30)) return reject(SDPA_EUNSUPPORTED);
         dim3 grid((unsigned)(8 * ((items + 7) / 8)), 1, 1);
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, st,

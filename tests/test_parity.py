@@ -66,6 +66,18 @@ def test_prefill_unequal_lengths(gpu_lib, lq, lk, mask_kind):
     assert_parity(run_gpu(c), oracle_out(c), "bf16", f"prefill Lq={lq} Lk={lk} {mask_kind}")
 
 
+# Wide heads: the query heads of one grouped-query group share a workgroup's
+# K/V tiles (up to 8 at a time), so group sizes that split that share in every
+# way are covered: 1, 3 (odd), 4, 8 and 12, with ragged row tiles and Lq != Lk.
+@pytest.mark.parametrize("hq,hkv", [(3, 3), (6, 2), (8, 2), (16, 2), (12, 1)])
+@pytest.mark.parametrize("mask_kind", ["none", "causal", "additive"])
+@pytest.mark.parametrize("D", [256, 512])
+def test_prefill_wide_head_groups(gpu_lib, D, mask_kind, hq, hkv):
+    c = si.make_case(1, hq, hkv, 70, 133, D, dtype="bf16", layout="bhld", mask_kind=mask_kind,
+                     seed=D + hq * 7 + hkv, mask_shape="qk", mask_p=0.2)
+    assert_parity(run_gpu(c), oracle_out(c), "bf16", f"prefill D={D} Hq={hq} Hkv={hkv} {mask_kind}")
+
+
 # --------------------------------------------------------------------------
 # Decode matrix (q_len <= 8 -> vector kernel, split keys + combine).
 # --------------------------------------------------------------------------
