@@ -21,7 +21,6 @@ cpu_baseline: the float64 oracle on the host, on a bounded sample.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -51,13 +50,21 @@ WORKLOADS = {
 PRIMARY = "decode-d256-lk4096"
 
 
-def kernel_hash() -> str:
-    """Hash of the kernel sources: counters taken on other sources are stale."""
+# kernel sources each workload's kernels are built from (counters taken on
+# other sources are stale)
+KERNEL_SOURCES = {
+    "decode": ["attn_common.h", "decode_kernel.h", "attn_kernel.h", "launch.h", "inst_template.hip.in"],
+    "prefill72": ["attn_common.h", "prefill_kernel.h", "launch.h", "inst_template.hip.in"],
+    "prefill512": ["attn_common.h", "prefill_wide_kernel.h", "launch.h", "inst_template.hip.in"],
+    "tiny": ["attn_common.h", "attn_kernel.h", "tile_configs.h", "launch.h", "inst_template.hip.in"],
+}
+
+
+def kernel_hash(name: str = PRIMARY) -> str:
+    """Hash of the sources of `name`'s kernels."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "scaled_dot_product_sdpa_amd", "csrc", "*"))):
-        if os.path.basename(p).startswith("sdpa_host"):
-            continue
-        h.update(open(p, "rb").read())
+    for f in KERNEL_SOURCES[WORKLOADS[name]["kind"]]:
+        h.update(open(os.path.join(ROOT, "scaled_dot_product_sdpa_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -233,7 +240,7 @@ def load_traffic(name: str):
     except Exception:
         return None
     ent = data.get("workloads", {}).get(name)
-    if not ent or ent.get("kernel_hash") != kernel_hash():
+    if not ent or ent.get("kernel_hash") != kernel_hash(name):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -249,11 +256,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile-run", action="store_true",
                     help="only run --steps eager calls of --workload (for rocprofv3), print nothing else")
+    ap.add_argument("--profile-copy", type=int, default=0, metavar="MIB",
+                    help="only run --steps device-to-device copies of MIB MiB (calibrates rocprofv3 byte counters)")
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the path shards by kv head across GPUs "
-                                   "(see the design notes), but no multi-GPU run is implemented",
+        print(json.dumps({"error": "one GPU only: a multi-GPU run (sharding by kv head) is not implemented",
                           "n_gpus": a.gpus}))
         sys.exit(2)
 
@@ -264,6 +272,16 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     sdpa.load()
+
+    if a.profile_copy:
+        n = a.profile_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(a.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] profile copy: {a.steps} x {n} bytes", flush=True)
+        return
 
     if a.profile_run:
         c = make_case(a.workload)
@@ -294,6 +312,7 @@ def main():
             secondary[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "eager_ms_per_step",
                                                  "kernel_ms", "combine_ms", "kernel_rate", "rate_unit",
                                                  "peak", "frac", "route")}
+            secondary[name]["traffic"] = load_traffic(name)
     cpu = None
     if not a.no_cpu:
         print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
@@ -311,7 +330,7 @@ def main():
         "config": prim["config"], "eager_ms_per_step": prim["eager_ms_per_step"],
         "timing": "HIP graph of K steps, replayed" if prim["graph_ms_per_step"] else "eager",
         "cold_cache_replicas": prim["replicas"], "route": prim["route"], "roofline": roof,
-        "cpu_baseline": cpu, "secondary": secondary, "kernel_hash": kernel_hash(),
+        "cpu_baseline": cpu, "secondary": secondary, "kernel_hash": kernel_hash(a.workload),
         "wall_s": round(time.time() - t_start, 1),
     }
     print(json.dumps(line), flush=True)
