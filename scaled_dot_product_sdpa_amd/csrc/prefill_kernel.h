@@ -47,6 +47,8 @@ struct PfCfg {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
+template <bool B> struct PfTag { static constexpr bool value = B; };
+
 template <class TR, class C, int MASK>
 __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) {
     constexpr int D = C::D, BN = C::BN, BM = C::BM;
@@ -181,6 +183,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
             const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
+            asm volatile("");  // keep this a branch, not a select on every tile
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -221,25 +224,23 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         }
     };
 
-    if (ntiles > 0) {
-        issue_tile(0, 0);
-        load_mask(0);
-    }
-    for (int it = 0; it < ntiles; ++it) {
+    // one key tile; the mask-free and the masked variants run as separate loops
+    // so neither carries the other's code (or register copies) around its body
+    auto tile = [&](int it, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
         const int kt = it * BN, stage = it & 1;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();  // tile `it` is in LDS; every wave is done with the other stage
         if (it + 1 < ntiles) issue_tile(kt + BN, stage ^ 1);
         f32x16_t sacc[C::NKB];
         scores(stage, sacc);
-        if (kt + BN <= kplain) {
+        if constexpr (!MASKED) {
             // no per-element mask: row max on unscaled scores
             float mx = NEG_INF;
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            if (it + 1 < ntiles) load_mask(kt + BN);
             softmax_pv(stage, sacc, mx * c_scale, c_scale);
         } else {
             float mtile = NEG_INF;
@@ -265,7 +266,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
             if (it + 1 < ntiles) load_mask(kt + BN);
             softmax_pv(stage, sacc, mtile, 1.f);
         }
+    };
+
+    int it = 0;
+    if (ntiles > 0) issue_tile(0, 0);
+    if constexpr (!HAS_MT) {
+        const int nplain = kplain / BN;
+        for (; it < nplain; ++it) tile(it, PfTag<false>{});
     }
+    if (it < ntiles) load_mask(it * BN);
+    for (; it < ntiles; ++it) tile(it, PfTag<true>{});
 
     // ---- epilogue ----
     float lsum_row;
