@@ -26,13 +26,20 @@ Sources (titles of the pages; section in brackets):
     n_rep per key/value head.
   * mlx PR #4330 "Support head dimension 72 in Metal full attention"
     [Proposed changes]: the mask kinds are none, additive, boolean, causal.
+  * mlx issue #3885 [Summary]: the d=256 model whose shapes drive the decode
+    configuration alternates "sliding" (local) layers with global ones; the
+    sliding kind here is that local attention.
 
 Readings where the pages are silent (each is also listed in the design notes):
   * boolean masks: true / nonzero = attend, false = masked (bias -inf);
   * causal masks are aligned bottom-right: query row i sits at key position
     i + (Lk - Lq), and attends to keys j <= that position;
   * an additive mask is added after the scale (it is not scaled);
-  * a row whose every key is masked has no defined softmax; its output is 0.
+  * a row whose every key is masked has no defined softmax; its output is 0;
+  * sliding (local) attention keeps the causal alignment and a window of W
+    keys: query i at position pos = i + (Lk - Lq) attends keys j with
+    pos - W < j <= pos (the page names the layer type, not its formula; this
+    is the usual local-causal window, the current key included).
 
 Parity pins for every function here live in tests/test_oracle.py.
 """
@@ -43,7 +50,7 @@ from typing import Iterable, Sequence
 
 import numpy as np
 
-MASK_KINDS = ("none", "additive", "boolean", "causal")
+MASK_KINDS = ("none", "additive", "boolean", "causal", "sliding")
 
 
 # --------------------------------------------------------------------------
@@ -78,6 +85,8 @@ def mask_bias(mask_kind: str, mask, q_len: int, kv_len: int) -> np.ndarray:
     additive -> the stored mask values, widened exactly to float64
     boolean  -> 0 where the mask is true (nonzero), -inf where it is false
     causal   -> 0 where key j <= i + (kv_len - q_len), else -inf
+    sliding  -> `mask` is the window W >= 1: 0 where pos - W < j <= pos with
+                pos = i + (kv_len - q_len), else -inf
     """
     if mask_kind == "none":
         return np.zeros((1, 1, 1, 1), dtype=np.float64)
@@ -90,6 +99,13 @@ def mask_bias(mask_kind: str, mask, q_len: int, kv_len: int) -> np.ndarray:
         pos = np.arange(q_len, dtype=np.int64)[:, None] + (kv_len - q_len)
         key = np.arange(kv_len, dtype=np.int64)[None, :]
         return np.where(key <= pos, 0.0, -np.inf)[None, None, :, :]
+    if mask_kind == "sliding":
+        window = int(mask)
+        if window < 1:
+            raise ValueError("sliding window must be >= 1")
+        pos = np.arange(q_len, dtype=np.int64)[:, None] + (kv_len - q_len)
+        key = np.arange(kv_len, dtype=np.int64)[None, :]
+        return np.where((key <= pos) & (key > pos - window), 0.0, -np.inf)[None, None, :, :]
     raise ValueError(f"unknown mask kind {mask_kind!r}")
 
 
@@ -151,10 +167,12 @@ def sdpa(q, k, v, scale: float, mask_kind: str = "none", mask=None,
     """softmax(scale * Q K^T + M) V with grouped-query heads, in float64.
 
     q: logical [B, Hq, Lq, D]; k: logical [B, Hkv, Lk, D]; v: logical
-    [B, Hkv, Lk, Dv] (Dv may differ from D; any real dtype, widened exactly).  mask: broadcastable to [B, Hq, Lq, Lk] for the
-    additive (float values) and boolean (nonzero = attend) kinds; ignored for
-    none and causal.  q_rows restricts the computation to those query rows
-    (all rows if None); row indices keep their meaning for the causal mask.
+    [B, Hkv, Lk, Dv] (Dv may differ from D; any real dtype, widened exactly).
+    mask: broadcastable to [B, Hq, Lq, Lk] for the additive (float values) and
+    boolean (nonzero = attend) kinds; the window W for the sliding kind;
+    ignored for none and causal.  q_rows restricts the computation to those
+    query rows (all rows if None); row indices keep their meaning for the
+    causal and sliding masks.
     Returns float64 [B, Hq, len(rows), Dv].
     """
     q, k, v, n_rep, bias = _prepare(q, k, v, mask_kind, mask)
@@ -242,7 +260,10 @@ def brute_force_sdpa(q, k, v, scale: float, mask_kind: str = "none", mask=None):
     B, Hq, Lq, D = q.shape
     Hkv, Lk, Dv = k.shape[1], k.shape[2], v.shape[3]
     n_rep = Hq // Hkv
-    if mask is not None:
+    window = None
+    if mask_kind == "sliding":
+        window = int(mask)
+    elif mask is not None:
         mask = np.broadcast_to(np.asarray(mask), (B, Hq, Lq, Lk))
     out = [[[[0.0] * Dv for _ in range(Lq)] for _ in range(Hq)] for _ in range(B)]
     for b in range(B):
@@ -257,6 +278,8 @@ def brute_force_sdpa(q, k, v, scale: float, mask_kind: str = "none", mask=None):
                     elif mask_kind == "boolean" and not mask[b, h, i, j]:
                         s = -math.inf
                     elif mask_kind == "causal" and j > i + (Lk - Lq):
+                        s = -math.inf
+                    elif mask_kind == "sliding" and not (i + (Lk - Lq) - window < j <= i + (Lk - Lq)):
                         s = -math.inf
                     scores.append(s)
                 top = max(scores)

@@ -66,8 +66,21 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     const int per = (total + 7) / 8;
     const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
     if (item >= total) return;
-    const int tt = item % nqt, bh = item / nqt;
-    const int qh = bh % p.Hq, b = bh / p.Hq;
+    // With a mask tensor, the heads of one row tile run next to each other on one
+    // XCD so its mask rows (usually shared by every head) are read from L2;
+    // otherwise the row tiles of one head do, sharing K and V.
+    int tt, qh, b;
+    if constexpr (HAS_MT) {
+        qh = item % p.Hq;
+        const int r = item / p.Hq;
+        tt = r % nqt;
+        b = r / nqt;
+    } else {
+        tt = item % nqt;
+        const int bh = item / nqt;
+        qh = bh % p.Hq;
+        b = bh / p.Hq;
+    }
     const int t = (MASK == MASK_CAUSAL) ? nqt - 1 - tt : tt;
     const int g = qh / p.n_rep;
     const int i0 = t * BM;

@@ -95,11 +95,24 @@ __global__ __launch_bounds__(C::NT, 1) void prefill_r16_kernel(const Params p) {
     const int per = (total + 7) / 8;
     const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
     if (item >= total) return;
-    const int tt = item % nrt;
-    int rest = item / nrt;
-    const int hgi = rest % nhg;
-    rest /= nhg;
-    const int g = rest % p.Hkv, b = rest / p.Hkv;
+    // with a mask tensor the head groups of one row tile run next to each other
+    // (mask rows shared through L2), otherwise the row tiles of one group do
+    int tt, hgi, g, b;
+    if constexpr (HAS_MT) {
+        hgi = item % nhg;
+        int rest = item / nhg;
+        g = rest % p.Hkv;
+        rest /= p.Hkv;
+        tt = rest % nrt;
+        b = rest / nrt;
+    } else {
+        tt = item % nrt;
+        int rest = item / nrt;
+        hgi = rest % nhg;
+        rest /= nhg;
+        g = rest % p.Hkv;
+        b = rest / p.Hkv;
+    }
     const int t = (MASK == MASK_CAUSAL) ? nrt - 1 - tt : tt;  // heavy row tiles first
     const int i0 = t * BMW;
     const int qh = g * n_rep + hgi * HG + (w % HG);

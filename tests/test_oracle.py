@@ -89,6 +89,8 @@ def test_oracle_matches_brute_force(mask_kind, lq, lk):
         mask = _rand((1, Hq, lq, lk), 4)
     elif mask_kind == "boolean":
         mask = si.rng(5).random((B, 1, lq, lk)) > 0.3
+    elif mask_kind == "sliding":
+        mask = 2
     ref = oracle.brute_force_sdpa(q, k, v, 0.37, mask_kind, mask)
     got = oracle.sdpa(q, k, v, 0.37, mask_kind, mask)
     np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-14)
@@ -113,6 +115,12 @@ def test_oracle_matches_torch_float64(mask_kind):
         kw["attn_mask"] = torch.from_numpy(mask)
     elif mask_kind == "causal":
         kw["is_causal"] = True
+    elif mask_kind == "sliding":
+        # torch has no sliding kind: keep the lower triangle minus everything
+        # W or more diagonals below it (Lq == Lk here)
+        mask = 5
+        ones = torch.ones(L, L, dtype=torch.bool)
+        kw["attn_mask"] = torch.tril(ones) & ~torch.tril(ones, diagonal=-mask)
     tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
     ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.21, enable_gqa=True, **kw)
     got = oracle.sdpa(q, k, v, 0.21, mask_kind, mask)
@@ -223,6 +231,34 @@ def test_gqa_equals_mha_with_repeated_kv():
     np.testing.assert_array_equal(a[:, 5:6], c)
 
 
+def test_sliding_window_closed_forms():
+    """W = 1 keeps one key (O = V[pos]); W >= every position is plain causal;
+    identical keys give the mean of V over the window (Lq < Lk: positions shift)."""
+    q, k, v = _rand((1, 2, 6, 4), 1), _rand((1, 1, 9, 4), 2), _rand((1, 1, 9, 4), 3)
+    off = 9 - 6
+    one = oracle.sdpa(q, k, v, 0.7, "sliding", 1)
+    for i in range(6):
+        np.testing.assert_allclose(one[0, :, i], np.broadcast_to(v[0, 0, i + off], (2, 4)), rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(oracle.sdpa(q, k, v, 0.7, "sliding", 9), oracle.sdpa(q, k, v, 0.7, "causal"))
+    np.testing.assert_array_equal(oracle.sdpa(q, k, v, 0.7, "sliding", 50), oracle.sdpa(q, k, v, 0.7, "causal"))
+    same = np.broadcast_to(k[:, :, :1], k.shape)
+    for w in (2, 4):
+        got = oracle.sdpa(q, same, v, 0.7, "sliding", w)
+        for i in range(6):
+            lo = max(0, i + off - w + 1)
+            np.testing.assert_allclose(got[0, 0, i], v[0, 0, lo:i + off + 1].mean(axis=0), rtol=1e-13, atol=1e-14)
+
+
+def test_sliding_window_chunks_match_the_block():
+    """Query chunks against the full key range, bottom-right aligned, equal the block."""
+    q, k, v = _rand((1, 2, 12, 4), 5), _rand((1, 2, 12, 4), 6), _rand((1, 2, 12, 4), 7)
+    full = oracle.sdpa(q, k, v, 0.5, "sliding", 4)
+    for s0 in range(0, 12, 5):
+        s1 = min(12, s0 + 5)
+        part = oracle.sdpa(q[:, :, s0:s1], k[:, :, :s1], v[:, :, :s1], 0.5, "sliding", 4)
+        np.testing.assert_allclose(part, full[:, :, s0:s1], rtol=1e-13, atol=1e-14)
+
+
 def test_constant_additive_shift_is_invariant():
     q, k, v = _rand((1, 2, 6, 4), 1), _rand((1, 2, 9, 4), 2), _rand((1, 2, 9, 4), 3)
     m = _rand((1, 1, 6, 9), 4)
@@ -276,7 +312,8 @@ def _pins_hold():
             test_p1_layout_bug_reproduces_printed_max_diff,
             test_gqa_equals_mha_with_repeated_kv,
             test_identical_keys_give_mean_of_v_and_causal_prefix_means,
-            test_one_hot_scores_do_not_overflow]
+            test_one_hot_scores_do_not_overflow,
+            test_sliding_window_closed_forms]
     pins += [lambda k=k: test_oracle_matches_torch_float64(k) for k in oracle.MASK_KINDS]
     pins += [lambda k=k: test_oracle_matches_brute_force(k, 3, 5) for k in oracle.MASK_KINDS]
     with np.errstate(all="ignore"):
@@ -294,7 +331,7 @@ def test_pins_hold_for_the_real_oracle():
 
 @pytest.mark.parametrize("mutation", ["no_scale", "softmax_over_queries", "reversed_v_rows",
                                       "head_modulo", "causal_top_left", "mask_dropped",
-                                      "mask_scaled", "no_max_shift"])
+                                      "mask_scaled", "no_max_shift", "sliding_window_plus_one"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     """Plant a plausible mistake in the oracle (CPU) and check that a pin fails."""
     if mutation == "no_scale":
@@ -330,6 +367,10 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
                             orig("none", None, lq, lk) if kind == "additive" else orig(kind, mask, lq, lk))
     elif mutation == "mask_scaled":
         monkeypatch.setattr(so, "_scores", lambda qh, kg, scale, b: (qh @ kg.T + b) * float(scale))
+    elif mutation == "sliding_window_plus_one":
+        orig = so.mask_bias
+        monkeypatch.setattr(so, "mask_bias", lambda kind, mask, lq, lk:
+                            orig(kind, int(mask) + 1, lq, lk) if kind == "sliding" else orig(kind, mask, lq, lk))
     elif mutation == "no_max_shift":
         monkeypatch.setattr(so, "_softmax_rows", lambda s: np.nan_to_num(
             np.exp(s) / np.exp(s).sum(-1, keepdims=True)))
