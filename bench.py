@@ -45,6 +45,8 @@ WORKLOADS = {
     "prefill-d72-boolean": dict(kind="prefill72", mask="boolean"),
     "prefill-d72-causal": dict(kind="prefill72", mask="causal"),
     "prefill-d512-causal": dict(kind="prefill512"),
+    "prefill-d256-sliding-w1024": dict(kind="sliding", q_len=4096, kv_len=4096, window=1024),
+    "decode-d256-sliding-w1024": dict(kind="sliding", q_len=1, kv_len=4096, window=1024),
     "tiny-f32": dict(kind="tiny"),
 }
 PRIMARY = "decode-d256-lk4096"
@@ -56,6 +58,8 @@ KERNEL_SOURCES = {
     "decode": ["attn_common.h", "decode_kernel.h", "attn_kernel.h", "launch.h", "inst_template.hip.in"],
     "prefill72": ["attn_common.h", "prefill_kernel.h", "launch.h", "inst_template.hip.in"],
     "prefill512": ["attn_common.h", "prefill_wide_kernel.h", "launch.h", "inst_template.hip.in"],
+    "sliding": ["attn_common.h", "prefill_wide_kernel.h", "decode_kernel.h", "attn_kernel.h", "launch.h",
+                "inst_template.hip.in"],
     "tiny": ["attn_common.h", "attn_kernel.h", "tile_configs.h", "launch.h", "inst_template.hip.in"],
 }
 
@@ -77,6 +81,8 @@ def make_case(name: str):
         return si.prefill72_case(w["mask"])
     if w["kind"] == "prefill512":
         return si.prefill512_case()
+    if w["kind"] == "sliding":
+        return si.sliding_case(w["q_len"], w["kv_len"], w["window"])
     return si.tiny_case("random")
 
 
@@ -88,12 +94,25 @@ def describe(name: str, c) -> dict:
 
 
 def work(c) -> tuple[float, str]:
-    """Algorithmic work of one call: K+V bytes for decode, flops for prefill."""
+    """Algorithmic work of one call: K+V bytes for decode, flops for prefill.
+
+    Causal prefill counts half the score matrix; a sliding window counts the
+    (query, key) pairs it keeps, and a sliding decode the keys any query reaches.
+    """
     d = c.dims
-    if d["q_len"] <= 8:
+    Lq, Lk = d["q_len"], d["kv_len"]
+    if Lq <= 8:
         es = c.k.element_size()
-        return 2.0 * d["batch"] * d["n_kv_heads"] * d["kv_len"] * d["head_dim"] * es, "bytes"
-    f = 4.0 * d["batch"] * d["n_q_heads"] * d["q_len"] * d["kv_len"] * d["head_dim"]
+        keys = Lk
+        if c.mask_kind == "sliding":
+            keys = min(Lk, c.meta["window"] + Lq - 1)
+        return 2.0 * d["batch"] * d["n_kv_heads"] * keys * d["head_dim"] * es, "bytes"
+    per_pair = 4.0 * d["batch"] * d["n_q_heads"] * d["head_dim"]
+    if c.mask_kind == "sliding":
+        w, off = c.meta["window"], Lk - Lq
+        pairs = sum(min(w, i + off + 1) for i in range(Lq))
+        return per_pair * pairs, "flops"
+    f = per_pair * Lq * Lk
     return (f / 2 if c.mask_kind == "causal" else f), "flops"
 
 
@@ -124,7 +143,8 @@ def measure(name: str, steps: int, warmup: int) -> dict:
 
     def step(i):
         q, k, v, m = reps[i % nrep]
-        sdpa.forward(q, k, v, scale=c.scale, mask=m, mask_kind=c.mask_kind, out=out, workspace=ws)
+        sdpa.forward(q, k, v, scale=c.scale, mask=m, mask_kind=c.mask_kind, out=out, workspace=ws,
+                     window=c.meta.get("window"))
 
     for i in range(warmup):
         step(i)
@@ -196,7 +216,9 @@ def cpu_baseline(name: str, budget_s: float) -> dict:
     c = make_case(name)
     amount, unit = work(c)
     mask = None
-    if c.mask is not None:
+    if c.mask_kind == "sliding":
+        mask = c.meta["window"]
+    elif c.mask is not None:
         mask = c.mask.double().numpy() if c.mask_kind == "additive" else c.mask.numpy()
     q, k, v = (t.double().numpy() for t in (c.q, c.k, c.v))
     Lq = q.shape[2]
@@ -293,7 +315,8 @@ def main():
                          dtype=torch.uint8, device="cuda")
         out = torch.empty(q.shape, dtype=q.dtype, device="cuda")
         for _ in range(a.steps):
-            sdpa.forward(q, k, v, scale=c.scale, mask=m, mask_kind=c.mask_kind, out=out, workspace=ws)
+            sdpa.forward(q, k, v, scale=c.scale, mask=m, mask_kind=c.mask_kind, out=out, workspace=ws,
+                         window=c.meta.get("window"))
         torch.cuda.synchronize()
         print(f"[bench] profile run: {a.steps} x {a.workload}", flush=True)
         return

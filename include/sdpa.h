@@ -70,6 +70,10 @@ typedef enum { SDPA_F32 = 0, SDPA_F16 = 1, SDPA_BF16 = 2, SDPA_U8 = 3 } sdpa_dty
  *   BOOLEAN   one byte per element: nonzero = attend (M = 0), zero = masked (M = -inf).
  *   CAUSAL    no tensor; bottom-right aligned: query i attends key j iff
  *             j <= i + (Lk - Lq).
+ *   SLIDING   no tensor; the causal mask limited to the `window` most recent
+ *             keys: query i at position pos = i + (Lk - Lq) attends key j iff
+ *             pos - window < j <= pos (the local layers of the d=256 model in
+ *             mlx issue #3885, "Summary").  Only sdpa_forward_sliding takes it.
  * Mask strides use the same logical (b, h, l, d) order with `d` meaning the key
  * index j; a zero stride broadcasts that axis; `h` indexes QUERY heads.
  * A query row whose every key is masked produces an all-zero output row. */
@@ -77,7 +81,8 @@ typedef enum {
     SDPA_MASK_NONE = 0,
     SDPA_MASK_ADDITIVE = 1,
     SDPA_MASK_BOOLEAN = 2,
-    SDPA_MASK_CAUSAL = 3
+    SDPA_MASK_CAUSAL = 3,
+    SDPA_MASK_SLIDING = 4
 } sdpa_mask_kind;
 
 /* Kernels (mlx issue #3885, "Current routing": vector for qL <= 8, full for qL > 8). */
@@ -115,9 +120,11 @@ typedef struct {
  *                  not overlap q, k, v or the workspace.
  *   batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim   all >= 1.
  *   scale          multiplies Q K^T (pass 1/sqrt(head_dim) for the usual scale).
- *   mask_kind      see sdpa_mask_kind.  `mask`, `mask_st` and `mask_dtype` are
- *                  read only for ADDITIVE (mask_dtype = dtype or SDPA_F32) and
- *                  BOOLEAN (mask_dtype = SDPA_U8); mask must then be non-null.
+ *   mask_kind      see sdpa_mask_kind (SLIDING: use sdpa_forward_sliding; here it
+ *                  is SDPA_EINVAL).  `mask`, `mask_st` and `mask_dtype` are read
+ *                  only for ADDITIVE (mask_dtype = SDPA_F32, SDPA_F16 or
+ *                  SDPA_BF16, any of them for any dtype) and BOOLEAN
+ *                  (mask_dtype = SDPA_U8); mask must then be non-null.
  *   workspace      device scratch of at least sdpa_workspace_size(...) bytes,
  *                  256-byte aligned (may be NULL when that size is 0).  The
  *                  vector kernel writes its per-split partial results there
@@ -138,6 +145,24 @@ int sdpa_forward(const void* q, sdpa_strides q_st,
                  sdpa_dtype mask_dtype,
                  void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/*
+ * sdpa_forward_sliding -- sdpa_forward with mask kind SLIDING: causal
+ * attention over the `window` (>= 1) most recent keys of each query
+ * (bottom-right aligned).  Same operands, workspace, stream and status codes
+ * as sdpa_forward; window < 1 is SDPA_EINVAL.  The full kernel skips the key
+ * tiles left of every row's window; the vector kernel splits only the keys
+ * the window can reach, so sdpa_workspace_size() for the same shape is enough.
+ */
+int sdpa_forward_sliding(const void* q, sdpa_strides q_st,
+                         const void* k, sdpa_strides k_st,
+                         const void* v, sdpa_strides v_st,
+                         void* out, sdpa_strides o_st,
+                         int batch, int q_len, int kv_len,
+                         int n_q_heads, int n_kv_heads, int head_dim,
+                         sdpa_dtype dtype, float scale, int window,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * sdpa_select_kernel -- the predicate sdpa_forward itself uses (one shared

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsdpa.so")
 
 SDPA_F32, SDPA_F16, SDPA_BF16, SDPA_U8 = 0, 1, 2, 3
-MASK_KINDS = {"none": 0, "additive": 1, "boolean": 2, "causal": 3}
+MASK_KINDS = {"none": 0, "additive": 1, "boolean": 2, "causal": 3, "sliding": 4}
 KERNELS = {0: "unsupported", 1: "full", 2: "vector"}
 STATUS = {0: "SDPA_OK", -1: "SDPA_EINVAL", -2: "SDPA_EUNSUPPORTED", -3: "SDPA_EWORKSPACE",
           -4: "SDPA_ELAUNCH", -5: "SDPA_EHIP"}
@@ -25,7 +25,7 @@ _TORCH_DT = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: S
              torch.uint8: SDPA_U8, torch.bool: SDPA_U8}
 
 # Every symbol include/sdpa.h declares (checked by the CPU test suite).
-EXPORTS = ("sdpa_forward", "sdpa_select_kernel", "sdpa_describe_route", "sdpa_workspace_size",
+EXPORTS = ("sdpa_forward", "sdpa_forward_sliding", "sdpa_select_kernel", "sdpa_describe_route", "sdpa_workspace_size",
            "sdpa_head_dims", "sdpa_strerror", "sdpa_last_hip_error", "sdpa_route_counters",
            "sdpa_timing_start", "sdpa_timing_stop")
 
@@ -57,6 +57,9 @@ def load(path: str = LIB_PATH):
         lib.sdpa_forward.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides,
                                      i, i, i, i, i, i, i, ctypes.c_float, i, vp, Strides, i, vp, sz, vp]
         lib.sdpa_forward.restype = i
+        lib.sdpa_forward_sliding.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides,
+                                             i, i, i, i, i, i, i, ctypes.c_float, i, vp, sz, vp]
+        lib.sdpa_forward_sliding.restype = i
         dims = [i, i, i, i, i, i, i]
         lib.sdpa_select_kernel.argtypes = dims + [i, ctypes.POINTER(i), ctypes.POINTER(i)]
         lib.sdpa_select_kernel.restype = i
@@ -183,14 +186,15 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
             mask: Optional[torch.Tensor] = None, mask_kind: Optional[str] = None,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-            layout: str = "bhld") -> torch.Tensor:
+            layout: str = "bhld", window: Optional[int] = None) -> torch.Tensor:
     """softmax(scale * q k^T + mask) v on the GPU through libsdpa.so.
 
     q: [B, Hq, Lq, D], k and v: [B, Hkv, Lk, D] in logical order (any strides,
     e.g. a transposed view of [B, L, H, D] storage); with layout="blhd" they
     are given in [B, L, H, D] order instead and the result is too.
     mask: broadcastable to [B, Hq, Lq, Lk]; bool/uint8 -> boolean, float ->
-    additive; mask_kind="causal" needs no tensor.
+    additive; mask_kind="causal" needs no tensor; mask_kind="sliding" takes
+    `window` (the number of most recent keys each query attends, >= 1).
     """
     lib = load()
     if layout == "blhd":
@@ -233,9 +237,16 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
     wptr = workspace.data_ptr() if workspace is not None else None
     wlen = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = lib.sdpa_forward(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
-                          out.data_ptr(), _strides(out), B, Lq, Lk, Hq, Hkv, D, dt, float(scale),
-                          mk, mptr, mst, mdt, wptr, wlen, stream)
+    if mask_kind == "sliding":
+        if window is None:
+            raise SdpaError(-1, "mask_kind=sliding needs window")
+        st = lib.sdpa_forward_sliding(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(),
+                                      _strides(v), out.data_ptr(), _strides(out), B, Lq, Lk, Hq, Hkv, D, dt,
+                                      float(scale), int(window), wptr, wlen, stream)
+    else:
+        st = lib.sdpa_forward(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+                              out.data_ptr(), _strides(out), B, Lq, Lk, Hq, Hkv, D, dt, float(scale),
+                              mk, mptr, mst, mdt, wptr, wlen, stream)
     if st != 0:
         raise SdpaError(st, f"sdpa_forward(B={B}, Lq={Lq}, Lk={Lk}, Hq={Hq}, Hkv={Hkv}, D={D}, {q.dtype}, "
                             f"{mask_kind})")

@@ -30,8 +30,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Kernel mask variants.  The C ABI's additive kind maps to MASK_ADD16
-// (bf16 / f16 mask) or MASK_ADD32 (float32 mask).
-enum { MASK_NONE = 0, MASK_ADD16 = 1, MASK_BOOL = 2, MASK_CAUSAL = 3, MASK_ADD32 = 4, MASK_VARIANTS = 5 };
+// (bf16 / f16 mask) or MASK_ADD32 (float32 mask); MASK_SLIDE is the causal
+// mask limited to a window of the most recent `window` keys.
+enum { MASK_NONE = 0, MASK_ADD16 = 1, MASK_BOOL = 2, MASK_CAUSAL = 3, MASK_ADD32 = 4, MASK_SLIDE = 5, MASK_VARIANTS = 6 };
+
+// key j is live for the query at position pos (= row + Lk - Lq) under MASK_SLIDE
+__device__ __forceinline__ bool in_window(int j, int pos, int window) { return j <= pos && j > pos - window; }
 enum { MDT_F32 = 0, MDT_F16 = 1, MDT_BF16 = 2, MDT_U8 = 3 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -56,6 +60,8 @@ struct Params {
     int splits;
     int keys_per_split;
     int col_groups;   // decode: column groups per kv head
+    int kbase;        // decode: first key of split 0 (keys before it are masked for every row)
+    int window;       // MASK_SLIDE: keys per query (>= 1)
 };
 
 template <class To, class From>

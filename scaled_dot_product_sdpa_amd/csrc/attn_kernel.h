@@ -108,7 +108,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void attn_tile_kernel(const Params p
         const int tt = item % nqt, bh = item / nqt;
         qh = bh % p.Hq;
         b = bh / p.Hq;
-        const int t = (MASK == MASK_CAUSAL) ? nqt - 1 - tt : tt;
+        const int t = (MASK == MASK_CAUSAL || MASK == MASK_SLIDE) ? nqt - 1 - tt : tt;
         g = qh / p.n_rep;
         const int i0 = t * BM;
         qmin = i0 + 32 * wm;
@@ -116,9 +116,13 @@ __global__ __launch_bounds__(C::NT, C::OCC) void attn_tile_kernel(const Params p
         rv = qi < p.Lq;
         kbeg = 0;
         kend = p.Lk;
-        if (MASK == MASK_CAUSAL) {
+        if (MASK == MASK_CAUSAL || MASK == MASK_SLIDE) {
             const int64_t e = (int64_t)i0 + BM + (p.Lk - p.Lq);
             kend = (int)(e < 0 ? 0 : (e > p.Lk ? p.Lk : e));
+        }
+        if (MASK == MASK_SLIDE) {  // first tile holding a key row i0 attends
+            const int lo = i0 + (p.Lk - p.Lq) - p.window + 1;
+            kbeg = min(kend, lo <= 0 ? 0 : (lo / BN) * BN);
         }
     } else {
         b = blockIdx.z;
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void attn_tile_kernel(const Params p
         qh = g * p.n_rep + rr / p.Lq;
         qi = rr % p.Lq;
         qmin = 0;
-        kbeg = split * p.keys_per_split;
+        kbeg = p.kbase + split * p.keys_per_split;
         kend = min(p.Lk, kbeg + p.keys_per_split);
     }
     const int off = p.Lk - p.Lq;  // bottom-right causal alignment
@@ -308,7 +312,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void attn_tile_kernel(const Params p
 
         // ---- tile max; per-element masking only where needed (wave-uniform test) ----
         const bool plain = !HAS_MT && p.scale_nonneg && (kt + BN <= kend) &&
-                           (MASK != MASK_CAUSAL || kt + BN - 1 <= qmin + off);
+                           (MASK != MASK_CAUSAL || kt + BN - 1 <= qmin + off) &&
+                           (MASK != MASK_SLIDE ||
+                            (!DECODE && kt + BN - 1 <= qmin + off && kt > min(qmin + 31, p.Lq - 1) + off - p.window));
         float mtile = NEG_INF;
         float c_eff;
         if (plain) {
@@ -332,6 +338,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void attn_tile_kernel(const Params p
                         if constexpr (MASK == MASK_ADD16 || MASK == MASK_ADD32)
                             x = __builtin_fmaf(mask_value<MASK>(mr[kb][a4], r, p.mask_dtype), kLog2e, x);
                         if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
+                        if constexpr (MASK == MASK_SLIDE) ok = ok && in_window(j, qi + off, p.window);
                         if constexpr (MASK == MASK_BOOL) ok = ok && ((mr[kb][a4] >> (8 * r)) & 0xffu) != 0u;
                         x = ok ? x : NEG_INF;
                         sacc[kb][4 * a4 + r] = x;

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
     const bool rv = r < p.n_rep * p.Lq;
     const int rr = rv ? r : 0;
     const int qh = grp * p.n_rep + rr / p.Lq, qi = rr % p.Lq;
-    const int kbeg = split * p.keys_per_split;
+    const int kbeg = p.kbase + split * p.keys_per_split;
     const int kend = min(p.Lk, kbeg + p.keys_per_split);
     const int off = p.Lk - p.Lq;
 
@@ -141,6 +141,7 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
             if constexpr (MASK == MASK_ADD16 || MASK == MASK_ADD32)
                 t = __builtin_fmaf(mask_value<MASK>(mr, e, p.mask_dtype), kLog2e, t);
             if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
+            if constexpr (MASK == MASK_SLIDE) ok = ok && in_window(j, qi + off, p.window);
             if constexpr (MASK == MASK_BOOL) ok = ok && ((mr >> (8 * e)) & 0xffu) != 0u;
             x[e] = ok ? t : NEG_INF;
             mx = fmaxf(mx, x[e]);

@@ -81,7 +81,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         qh = bh % p.Hq;
         b = bh / p.Hq;
     }
-    const int t = (MASK == MASK_CAUSAL) ? nqt - 1 - tt : tt;
+    constexpr bool CAUSAL_END = (MASK == MASK_CAUSAL || MASK == MASK_SLIDE);
+    const int t = CAUSAL_END ? nqt - 1 - tt : tt;
     const int g = qh / p.n_rep;
     const int i0 = t * BM;
     const int qmin = i0 + 32 * wm;  // first query row of this wave
@@ -89,16 +90,24 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     const bool rv = qi < p.Lq;
     const int off = p.Lk - p.Lq;
     int kend = p.Lk;
-    if (MASK == MASK_CAUSAL) {
+    if (CAUSAL_END) {
         const int64_t e = (int64_t)i0 + BM + off;
         kend = (int)(e < 0 ? 0 : (e > p.Lk ? p.Lk : e));
     }
-    // keys [0, kplain) need no per-element mask for any row of this wave
-    int kplain = kend;
-    if (MASK == MASK_CAUSAL) kplain = min(kend, max(0, qmin + off + 1));
-    if (HAS_MT || !p.scale_nonneg) kplain = 0;
-    kplain = (kplain / BN) * BN;  // whole tiles only
     const int ntiles = (kend + BN - 1) / BN;
+    // key tiles [t0, ntiles) hold every key some row of this workgroup attends;
+    // tiles [tp0, tp1) need no per-element mask for any row of this wave
+    int t0 = 0;
+    if (MASK == MASK_SLIDE) t0 = min(ntiles, max(0, i0 + off - p.window + 1) / BN);
+    int tp0 = t0, tp1 = kend / BN;
+    if (CAUSAL_END) tp1 = min(tp1, max(0, qmin + off + 1) / BN);
+    if (MASK == MASK_SLIDE) {
+        const int lo = min(qmin + 31, p.Lq - 1) + off - p.window + 1;  // window's left edge, wave's last row
+        tp0 = max(t0, lo <= 0 ? 0 : (lo + BN - 1) / BN);
+    }
+    if (HAS_MT || !p.scale_nonneg) tp1 = tp0;
+    tp0 = min(tp0, ntiles);
+    tp1 = max(tp0, min(tp1, ntiles));
 
     // ---- buffer resources over this (batch, kv head)'s K and V rows ----
     const int64_t kstep = (int64_t)p.ks[2] * 2, vstep = (int64_t)p.vs[2] * 2;
@@ -269,6 +278,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
                         if constexpr (MASK == MASK_ADD16 || MASK == MASK_ADD32)
                             x = __builtin_fmaf(mask_value<MASK>(mr[kb][a4], r, p.mask_dtype), kLog2e, x);
                         if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
+                        if constexpr (MASK == MASK_SLIDE) ok = ok && in_window(j, qi + off, p.window);
                         if constexpr (MASK == MASK_BOOL) ok = ok && ((mr[kb][a4] >> (8 * r)) & 0xffu) != 0u;
                         x = ok ? x : NEG_INF;
                         sacc[kb][4 * a4 + r] = x;
@@ -281,11 +291,13 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         }
     };
 
-    int it = 0;
-    if (ntiles > 0) issue_tile(0, 0);
+    // masked tiles left of the plain range (window edge), plain tiles, masked
+    // tiles right of it (diagonal, ragged end, or every tile of a mask tensor)
+    int it = t0;
+    if (it < ntiles) issue_tile(it * BN, it & 1);
     if constexpr (!HAS_MT) {
-        const int nplain = kplain / BN;
-        for (; it < nplain; ++it) tile(it, PfTag<false>{});
+        for (; it < tp0; ++it) tile(it, PfTag<true>{});
+        for (; it < tp1; ++it) tile(it, PfTag<false>{});
     }
     if (it < ntiles) load_mask(it * BN);
     for (; it < ntiles; ++it) tile(it, PfTag<true>{});

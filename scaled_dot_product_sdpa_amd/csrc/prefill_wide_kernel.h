@@ -113,7 +113,8 @@ __global__ __launch_bounds__(C::NT, 1) void prefill_r16_kernel(const Params p) {
         g = rest % p.Hkv;
         b = rest / p.Hkv;
     }
-    const int t = (MASK == MASK_CAUSAL) ? nrt - 1 - tt : tt;  // heavy row tiles first
+    constexpr bool CAUSAL_END = (MASK == MASK_CAUSAL || MASK == MASK_SLIDE);
+    const int t = CAUSAL_END ? nrt - 1 - tt : tt;  // heavy row tiles first
     const int i0 = t * BMW;
     const int qh = g * n_rep + hgi * HG + (w % HG);
     const int qmin = i0 + 16 * (w / HG);
@@ -121,15 +122,24 @@ __global__ __launch_bounds__(C::NT, 1) void prefill_r16_kernel(const Params p) {
     const bool rv = qi < p.Lq;
     const int off = p.Lk - p.Lq;
     int kend = p.Lk;
-    if (MASK == MASK_CAUSAL) {
+    if (CAUSAL_END) {
         const int64_t e = (int64_t)i0 + BMW + off;
         kend = (int)(e < 0 ? 0 : (e > p.Lk ? p.Lk : e));
     }
-    int kplain = kend;
-    if (MASK == MASK_CAUSAL) kplain = min(kend, max(0, qmin + off + 1));
-    if (HAS_MT || !p.scale_nonneg) kplain = 0;
-    const int nplain = kplain / BN;
     const int ntiles = (kend + BN - 1) / BN;
+    // key tiles [t0, ntiles) hold every key some row of this workgroup attends;
+    // tiles [tp0, tp1) need no per-element mask for any row of this wave
+    int t0 = 0;
+    if (MASK == MASK_SLIDE) t0 = min(ntiles, max(0, i0 + off - p.window + 1) / BN);
+    int tp0 = t0, tp1 = kend / BN;
+    if (CAUSAL_END) tp1 = min(tp1, max(0, qmin + off + 1) / BN);
+    if (MASK == MASK_SLIDE) {
+        const int lo = min(qmin + 15, p.Lq - 1) + off - p.window + 1;  // window's left edge, wave's last row
+        tp0 = max(t0, lo <= 0 ? 0 : (lo + BN - 1) / BN);
+    }
+    if (HAS_MT || !p.scale_nonneg) tp1 = tp0;
+    tp0 = min(tp0, ntiles);
+    tp1 = max(tp0, min(tp1, ntiles));
 
     const uint32_t kstep = (uint32_t)p.ks[2] * 2u, vstep = (uint32_t)p.vs[2] * 2u;
     const char* kglob = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)g * p.ks[1]) * 2;
@@ -258,6 +268,7 @@ __global__ __launch_bounds__(C::NT, 1) void prefill_r16_kernel(const Params p) {
                     if constexpr (MASK == MASK_ADD16 || MASK == MASK_ADD32)
                         x = __builtin_fmaf(mask_value<MASK>(mr[kb], r, p.mask_dtype), kLog2e, x);
                     if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
+                    if constexpr (MASK == MASK_SLIDE) ok = ok && in_window(j, qi + off, p.window);
                     if constexpr (MASK == MASK_BOOL) ok = ok && ((mr[kb] >> (8 * r)) & 0xffu) != 0u;
                     x = ok ? x : NEG_INF;
                     sacc[kb][r] = x;
@@ -323,10 +334,11 @@ __global__ __launch_bounds__(C::NT, 1) void prefill_r16_kernel(const Params p) {
         }
     };
 
-    int it = 0;
-    if (ntiles > 0) issue_tile(0, 0);
+    int it = t0;
+    if (it < ntiles) issue_tile(it * BN, it & 1);
     if constexpr (!HAS_MT) {
-        for (; it < nplain; ++it) tile(it, WideTag<false>{});
+        for (; it < tp0; ++it) tile(it, WideTag<true>{});
+        for (; it < tp1; ++it) tile(it, WideTag<false>{});
     }
     for (; it < ntiles; ++it) tile(it, WideTag<true>{});
 

@@ -82,7 +82,7 @@ int select(int batch, int q_len, int kv_len, int hq, int hkv, int d, sdpa_dtype 
     } else if (hq % hkv != 0) {
         why = SDPA_REASON_GROUPS;
         st = SDPA_EINVAL;
-    } else if (mk < SDPA_MASK_NONE || mk > SDPA_MASK_CAUSAL) {
+    } else if (mk < SDPA_MASK_NONE || mk > SDPA_MASK_SLIDING) {
         why = SDPA_REASON_MASK;
         st = SDPA_EINVAL;
     } else if (dt != SDPA_F32 && dt != SDPA_F16 && dt != SDPA_BF16) {
@@ -177,6 +177,7 @@ const char* mask_name(sdpa_mask_kind mk) {
         case SDPA_MASK_ADDITIVE: return "additive";
         case SDPA_MASK_BOOLEAN: return "boolean";
         case SDPA_MASK_CAUSAL: return "causal";
+        case SDPA_MASK_SLIDING: return "sliding";
     }
     return "?";
 }
@@ -342,12 +343,13 @@ int sdpa_route_counters(uint64_t* out, int n) {
     return 4;
 }
 
-int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
+namespace {
+
+int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
                  sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len, int n_q_heads,
                  int n_kv_heads, int head_dim, sdpa_dtype dtype, float scale, sdpa_mask_kind mask_kind,
-                 const void* mask, sdpa_strides mask_st, sdpa_dtype mask_dtype, void* workspace,
+                 const void* mask, sdpa_strides mask_st, sdpa_dtype mask_dtype, int window, void* workspace,
                  size_t workspace_bytes, void* stream) {
-    g_counters[0].fetch_add(1, std::memory_order_relaxed);
     sdpa_kernel kern;
     int reason;
     int st = select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, &kern, &reason);
@@ -414,12 +416,15 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     p.n_rep = n_q_heads / n_kv_heads;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);
     p.scale_nonneg = scale >= 0.f;
+    p.window = window;
+    p.kbase = 0;
 
     const KernelSet* ks = kernel_set(dtype, head_dim);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // kernel mask variant: the additive kind splits by mask element width
     int mk = (int)mask_kind;
     if (mask_kind == SDPA_MASK_ADDITIVE) mk = (mask_dtype == SDPA_F32) ? sdpa_dev::MASK_ADD32 : sdpa_dev::MASK_ADD16;
+    if (mask_kind == SDPA_MASK_SLIDING) mk = sdpa_dev::MASK_SLIDE;
     // optional per-kernel timing (diagnostics): events bracket each launch on `s`
     int tcall = -1;
     if (g_timing.used < g_timing.armed) tcall = g_timing.used++;
@@ -458,7 +463,13 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
 
     // vector (decode): split keys, then combine the splits
     const auto& t = ks->dec_cfg;
-    const DecodePlan plan = decode_plan(batch, q_len, kv_len, n_q_heads, n_kv_heads, t);
+    // a sliding window reaches no key left of (first row's position - window + 1):
+    // split only the keys from there on
+    if (mask_kind == SDPA_MASK_SLIDING) {
+        const long lo = (long)(kv_len - q_len) - window + 1;
+        p.kbase = lo > 0 ? (int)lo : 0;
+    }
+    const DecodePlan plan = decode_plan(batch, q_len, kv_len - p.kbase, n_q_heads, n_kv_heads, t);
     const size_t need = decode_ws_bytes(batch, q_len, n_q_heads, head_dim, plan);
     if (!workspace || workspace_bytes < need) return reject(SDPA_EWORKSPACE);
     if (((uintptr_t)workspace) % 256 != 0) return reject(SDPA_EINVAL);
@@ -484,6 +495,31 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     mark(2);
     g_counters[2].fetch_add(1, std::memory_order_relaxed);
     return SDPA_OK;
+}
+
+}  // namespace
+
+int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
+                 sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len, int n_q_heads,
+                 int n_kv_heads, int head_dim, sdpa_dtype dtype, float scale, sdpa_mask_kind mask_kind,
+                 const void* mask, sdpa_strides mask_st, sdpa_dtype mask_dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    g_counters[0].fetch_add(1, std::memory_order_relaxed);
+    if (mask_kind == SDPA_MASK_SLIDING) return reject(SDPA_EINVAL);  // needs a window: sdpa_forward_sliding
+    return forward_impl(q, q_st, k, k_st, v, v_st, out, o_st, batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
+                        dtype, scale, mask_kind, mask, mask_st, mask_dtype, 0, workspace, workspace_bytes, stream);
+}
+
+int sdpa_forward_sliding(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
+                         sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len,
+                         int n_q_heads, int n_kv_heads, int head_dim, sdpa_dtype dtype, float scale, int window,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    g_counters[0].fetch_add(1, std::memory_order_relaxed);
+    if (window < 1) return reject(SDPA_EINVAL);
+    const sdpa_strides none{0, 0, 0, 0};
+    return forward_impl(q, q_st, k, k_st, v, v_st, out, o_st, batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
+                        dtype, scale, SDPA_MASK_SLIDING, nullptr, none, SDPA_F32, window, workspace, workspace_bytes,
+                        stream);
 }
 
 }  // extern "C"

@@ -79,8 +79,10 @@ def linspace_block(shape) -> np.ndarray:
 
 def make_case(B, Hq, Hkv, Lq, Lk, D, dtype="bf16", layout="bhld", mask_kind="none",
               seed=0, std=1.0, scale=None, mask_p=None, mask_shape="key",
-              mask_dtype=None, name="") -> Case:
+              mask_dtype=None, name="", window=None) -> Case:
     """Seeded random case.
+
+    window: keys per query for mask_kind="sliding" (kept in meta["window"]).
 
     mask_shape for additive / boolean masks: "key" -> [1,1,1,Lk];
     "qk" -> [1,1,Lq,Lk]; "full" -> [B,Hq,Lq,Lk].
@@ -107,8 +109,12 @@ def make_case(B, Hq, Hkv, Lq, Lk, D, dtype="bf16", layout="bhld", mask_kind="non
             mask = torch.from_numpy(np.where(hit, np.float32(-1e9), np.float32(0.0))).to(mdt)
         else:
             mask = torch.from_numpy((~hit).astype(np.uint8))
-    return Case(q, k, v, float(scale), mask_kind, mask, layout, name,
-                dict(seed=seed, dtype=dtype, std=std))
+    meta = dict(seed=seed, dtype=dtype, std=std)
+    if mask_kind == "sliding":
+        if window is None or int(window) < 1:
+            raise ValueError("a sliding case needs window >= 1")
+        meta["window"] = int(window)
+    return Case(q, k, v, float(scale), mask_kind, mask, layout, name, meta)
 
 
 def tiny_case(variant="random", transposed=False) -> Case:
@@ -157,6 +163,14 @@ def prefill512_case(seq=4096, dtype="bf16") -> Case:
     """bf16 prefill B=1, Hq=32, Hkv=4, D=512, Lq=Lk=seq, causal, [B,H,L,D]."""
     return make_case(1, 32, 4, seq, seq, 512, dtype=dtype, layout="bhld", mask_kind="causal",
                      seed=5, name=f"prefill-d512-causal-L{seq}")
+
+
+def sliding_case(q_len=4096, kv_len=4096, window=1024, dtype="bf16") -> Case:
+    """bf16 sliding-window (local causal) attention with the shapes of the d=256
+    local layers named in mlx issue #3885 [Summary]: B=1, Hq=32, Hkv=16, D=256,
+    [B,H,L,D]; q_len=1 is a decode step over a kv_len cache (seed 6)."""
+    return make_case(1, 32, 16, q_len, kv_len, 256, dtype=dtype, layout="bhld", mask_kind="sliding",
+                     seed=6, window=window, name=f"sliding-d256-q{q_len}-k{kv_len}-w{window}")
 
 
 def to_device(case: Case, device="cuda"):

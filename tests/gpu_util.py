@@ -17,6 +17,8 @@ to_device = si.to_device
 def run_gpu(case: si.Case, **kw):
     import scaled_dot_product_sdpa_amd as sdpa
     q, k, v, mask = to_device(case)
+    if case.mask_kind == "sliding":
+        kw.setdefault("window", case.meta["window"])
     out = sdpa.forward(q, k, v, scale=case.scale, mask=mask, mask_kind=case.mask_kind, **kw)
     torch.cuda.synchronize()
     return out
@@ -24,7 +26,9 @@ def run_gpu(case: si.Case, **kw):
 
 def oracle_out(case: si.Case, q_rows=None):
     mask = None
-    if case.mask is not None:
+    if case.mask_kind == "sliding":
+        mask = case.meta["window"]
+    elif case.mask is not None:
         mask = case.mask.double().numpy() if case.mask_kind == "additive" else case.mask.numpy()
     return oracle.sdpa(case.q.double().numpy(), case.k.double().numpy(), case.v.double().numpy(),
                        np.float32(case.scale), case.mask_kind, mask, q_rows=q_rows)

@@ -61,7 +61,7 @@ def test_unsupported_is_an_error_with_a_reason(lib, args, reason, status):
 def test_every_dtype_and_head_dim_is_fused(lib):
     for d in sdpa.head_dims():
         for dt in (0, 1, 2):
-            for mk in ("none", "additive", "boolean", "causal"):
+            for mk in ("none", "additive", "boolean", "causal", "sliding"):
                 assert sdpa.select_kernel(2, 100, 100, 8, 2, d, dt, mk)[0] == "full"
                 assert sdpa.select_kernel(2, 1, 100, 8, 2, d, dt, mk)[0] == "vector"
 
@@ -120,7 +120,13 @@ def test_forward_rejects_bad_arguments_before_touching_the_gpu(lib):
     assert _forward(lib, mk=1, mask=4096 * 64, mdt=3) == -1            # additive mask can't be u8
     assert _forward(lib, mk=7) == -1                                   # unknown mask kind
     assert _forward(lib, o=1 << 20, dims=(1, 1, 16, 2, 2, 64), ws=None, wsb=0) == -3  # decode workspace
+    assert _forward(lib, mk=4) == -1                                   # sliding needs the window entry point
+    st = S(2 * 16 * 64, 16 * 64, 64, 1)
+    assert lib.sdpa_forward_sliding(4096, st, 4096, st, 4096, st, 1 << 20, st, 2, 16, 16, 16, 16, 64, 2, 0.125,
+                                    0, None, 0, None) == -1            # window < 1
+    assert lib.sdpa_forward_sliding(4096, st, 4096, st, 4096, st, 1 << 20, st, 2, 16, 16, 16, 16, 48, 2, 0.125,
+                                    4, None, 0, None) == -2            # head dim not built
     after = sdpa.route_counters()
-    assert after["calls"] - before["calls"] == 13
-    assert after["rejected"] - before["rejected"] == 13
+    assert after["calls"] - before["calls"] == 16
+    assert after["rejected"] - before["rejected"] == 16
     assert after["calls"] == after["full"] + after["vector"] + after["rejected"]

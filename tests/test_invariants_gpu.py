@@ -19,6 +19,23 @@ def test_causal_row0_is_v0_bitwise(gpu_lib, D, dtype):
     assert torch.equal(out[:, :, 0:1], v0)
 
 
+@pytest.mark.parametrize("lq,D,dtype", [(100, 72, "bf16"), (100, 512, "f16"), (100, 64, "f32"),
+                                        (1, 256, "bf16"), (6, 128, "f32")])
+def test_sliding_window_of_one_key_is_that_v_row_bitwise(gpu_lib, lq, D, dtype):
+    """W = 1: every query keeps exactly its own position's key, so P = 1 and O = V[pos]."""
+    c = si.make_case(1, 4, 2, lq, 130, D, dtype=dtype, mask_kind="sliding", seed=9, window=1)
+    out = run_gpu(c).cpu()
+    want = c.v[:, :, 130 - lq:].repeat_interleave(2, dim=1)
+    assert torch.equal(out, want)
+
+
+@pytest.mark.parametrize("lq,D,dtype", [(150, 72, "bf16"), (150, 256, "bf16"), (150, 80, "f32"), (3, 128, "bf16")])
+def test_sliding_window_covering_every_key_is_causal_bitwise(gpu_lib, lq, D, dtype):
+    c = si.make_case(1, 4, 2, lq, 300, D, dtype=dtype, mask_kind="sliding", seed=21, window=300)
+    causal = si.Case(c.q, c.k, c.v, c.scale, "causal", None, c.layout)
+    assert torch.equal(run_gpu(c), run_gpu(causal))
+
+
 @pytest.mark.parametrize("lq", [1, 200])
 def test_layout_permutation_is_bitwise_identical(gpu_lib, lq):
     a = si.make_case(1, 8, 4, lq, 300, 72, dtype="bf16", layout="blhd", mask_kind="causal", seed=11)

@@ -136,3 +136,35 @@ def test_prefill_d512_full_size_sampled_rows(gpu_lib):
 def test_prefill_d512_reduced_seq_all_rows(gpu_lib):
     c = si.prefill512_case(seq=300)
     assert_parity(run_gpu(c), oracle_out(c), "bf16", c.name)
+
+
+# --------------------------------------------------------------------------
+# Sliding-window (local causal) attention: windows from one key to more than
+# the whole sequence, tiles that start left of, straddle and sit inside the
+# window, Lq < Lk (a key-value cache in front of the queries), GQA.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("window", [1, 7, 64, 100, 1000])
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("D", HEAD_DIMS)
+def test_prefill_sliding_window(gpu_lib, D, dtype, window):
+    c = si.make_case(1, 4, 2, 190, 230, D, dtype=dtype, layout="bhld", mask_kind="sliding",
+                     seed=D + window, window=window)
+    assert_parity(run_gpu(c), oracle_out(c), dtype, f"prefill sliding D={D} {dtype} W={window}")
+
+
+@pytest.mark.parametrize("lq", [1, 5])
+@pytest.mark.parametrize("window", [1, 33, 300, 5000])
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+def test_decode_sliding_window(gpu_lib, D, window, lq):
+    for dtype in ("bf16", "f32"):
+        c = si.make_case(1, 8, 2, lq, 4100, D, dtype=dtype, layout="bhld", mask_kind="sliding",
+                         seed=D + window + lq, window=window)
+        assert_parity(run_gpu(c), oracle_out(c), dtype, f"decode sliding D={D} {dtype} W={window} Lq={lq}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(3, 3), (16, 2), (12, 1)])
+@pytest.mark.parametrize("D", [256, 512])
+def test_prefill_sliding_window_wide_groups(gpu_lib, D, hq, hkv):
+    c = si.make_case(1, hq, hkv, 150, 150, D, dtype="bf16", layout="bhld", mask_kind="sliding",
+                     seed=D + hq, window=45)
+    assert_parity(run_gpu(c), oracle_out(c), "bf16", f"prefill sliding D={D} Hq={hq} Hkv={hkv}")
