@@ -47,6 +47,7 @@ WORKLOADS = {
     "prefill-d512-causal": dict(kind="prefill512"),
     "prefill-d256-sliding-w1024": dict(kind="sliding", q_len=4096, kv_len=4096, window=1024),
     "decode-d256-sliding-w1024": dict(kind="sliding", q_len=1, kv_len=4096, window=1024),
+    "decode-qk192-v128-lk4096": dict(kind="decode_dv", Lk=4096),
     "tiny-f32": dict(kind="tiny"),
 }
 PRIMARY = "decode-d256-lk4096"
@@ -60,6 +61,7 @@ KERNEL_SOURCES = {
     "prefill512": ["attn_common.h", "prefill_wide_kernel.h", "launch.h", "inst_template.hip.in"],
     "sliding": ["attn_common.h", "prefill_wide_kernel.h", "decode_kernel.h", "attn_kernel.h", "launch.h",
                 "inst_template.hip.in"],
+    "decode_dv": ["attn_common.h", "decode_kernel.h", "attn_kernel.h", "launch.h", "inst_pair_template.hip.in"],
     "tiny": ["attn_common.h", "attn_kernel.h", "tile_configs.h", "launch.h", "inst_template.hip.in"],
 }
 
@@ -83,6 +85,8 @@ def make_case(name: str):
         return si.prefill512_case()
     if w["kind"] == "sliding":
         return si.sliding_case(w["q_len"], w["kv_len"], w["window"])
+    if w["kind"] == "decode_dv":
+        return si.decode_dv_case(w["Lk"])
     return si.tiny_case("random")
 
 
@@ -90,6 +94,7 @@ def describe(name: str, c) -> dict:
     d = c.dims
     return {"workload": name, "batch": d["batch"], "q_len": d["q_len"], "kv_len": d["kv_len"],
             "n_q_heads": d["n_q_heads"], "n_kv_heads": d["n_kv_heads"], "head_dim": d["head_dim"],
+            "v_head_dim": int(c.v.shape[3]),
             "mask": c.mask_kind, "layout": c.layout, "dtype": str(c.q.dtype).replace("torch.", "")}
 
 
@@ -106,7 +111,7 @@ def work(c) -> tuple[float, str]:
         keys = Lk
         if c.mask_kind == "sliding":
             keys = min(Lk, c.meta["window"] + Lq - 1)
-        return 2.0 * d["batch"] * d["n_kv_heads"] * keys * d["head_dim"] * es, "bytes"
+        return float(d["batch"] * d["n_kv_heads"] * keys * (d["head_dim"] + c.v.shape[3]) * es), "bytes"
     per_pair = 4.0 * d["batch"] * d["n_q_heads"] * d["head_dim"]
     if c.mask_kind == "sliding":
         w, off = c.meta["window"], Lk - Lq
@@ -135,10 +140,10 @@ def measure(name: str, steps: int, warmup: int) -> dict:
     nrep = max(2, -(-COLD_BYTES // kv_bytes)) if decode else 1
     reps = to_device_replicas(c, nrep)
     q0 = reps[0][0]
-    out = torch.empty(q0.shape, dtype=q0.dtype, device="cuda")
+    out = torch.empty(q0.shape[:3] + (c.v.shape[3],), dtype=q0.dtype, device="cuda")
     d = c.dims
     ws_bytes = sdpa.workspace_size(d["batch"], d["q_len"], d["kv_len"], d["n_q_heads"], d["n_kv_heads"],
-                                   d["head_dim"], q0.dtype)
+                                   d["head_dim"], q0.dtype, v_head_dim=c.v.shape[3])
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
 
     def step(i):
@@ -191,7 +196,7 @@ def measure(name: str, steps: int, warmup: int) -> dict:
         print(f"[bench] graph capture failed: {ex}", file=sys.stderr)
     ms = graph_ms if graph_ms is not None else eager_ms
     route = sdpa.describe_route(d["batch"], d["q_len"], d["kv_len"], d["n_q_heads"], d["n_kv_heads"],
-                                d["head_dim"], q0.dtype, c.mask_kind)
+                                d["head_dim"], q0.dtype, c.mask_kind, v_head_dim=c.v.shape[3])
     res = dict(config=describe(name, c), route=route, ms_per_step=ms, eager_ms_per_step=eager_ms,
                graph_ms_per_step=graph_ms, kernel_ms=kernel_ms, kernel_ms_p10=k_ms[len(k_ms) // 10],
                kernel_ms_p90=k_ms[(9 * len(k_ms)) // 10], combine_ms=combine_ms, replicas=nrep,
@@ -311,9 +316,10 @@ def main():
         q, k, v, m = si.to_device(c)
         d = c.dims
         ws = torch.empty(max(256, sdpa.workspace_size(d["batch"], d["q_len"], d["kv_len"], d["n_q_heads"],
-                                                       d["n_kv_heads"], d["head_dim"], q.dtype)),
+                                                       d["n_kv_heads"], d["head_dim"], q.dtype,
+                                                       v_head_dim=c.v.shape[3])),
                          dtype=torch.uint8, device="cuda")
-        out = torch.empty(q.shape, dtype=q.dtype, device="cuda")
+        out = torch.empty(q.shape[:3] + (c.v.shape[3],), dtype=q.dtype, device="cuda")
         for _ in range(a.steps):
             sdpa.forward(q, k, v, scale=c.scale, mask=m, mask_kind=c.mask_kind, out=out, workspace=ws,
                          window=c.meta.get("window"))

@@ -111,6 +111,7 @@ typedef struct {
 #define SDPA_REASON_GROUPS 3     /* n_q_heads is not a multiple of n_kv_heads  */
 #define SDPA_REASON_SIZE 4       /* a size is non-positive or too large        */
 #define SDPA_REASON_MASK 5       /* unknown mask kind                          */
+#define SDPA_REASON_V_HEAD_DIM 6 /* v_head_dim != head_dim outside the built pairs (see sdpa_forward_ex) */
 
 /*
  * sdpa_forward -- O = softmax(scale * Q K^T + M) V.
@@ -165,6 +166,32 @@ int sdpa_forward_sliding(const void* q, sdpa_strides q_st,
                          void* stream);
 
 /*
+ * sdpa_forward_ex -- the general call: sdpa_forward plus a V head dim and the
+ * sliding window.
+ *   v_head_dim     head dim of V and of `out` (and of their strides' extents).
+ *                  Equal to head_dim for every built head dim; the one distinct
+ *                  pairing built is head_dim 192 with v_head_dim 128, for the
+ *                  vector (decode, q_len <= 8) kernel and 16-bit types (the
+ *                  pairing mlx issue #3885 lists for its vector kernel under
+ *                  "Current routing").  Other pairings: SDPA_EUNSUPPORTED,
+ *                  reason SDPA_REASON_V_HEAD_DIM.
+ *   window         keys per query when mask_kind is SDPA_MASK_SLIDING (>= 1,
+ *                  else SDPA_EINVAL); ignored for the other kinds.
+ * Everything else as sdpa_forward; the workspace is sdpa_workspace_size_ex().
+ */
+int sdpa_forward_ex(const void* q, sdpa_strides q_st,
+                    const void* k, sdpa_strides k_st,
+                    const void* v, sdpa_strides v_st,
+                    void* out, sdpa_strides o_st,
+                    int batch, int q_len, int kv_len,
+                    int n_q_heads, int n_kv_heads, int head_dim, int v_head_dim,
+                    sdpa_dtype dtype, float scale,
+                    sdpa_mask_kind mask_kind, const void* mask, sdpa_strides mask_st,
+                    sdpa_dtype mask_dtype, int window,
+                    void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
  * sdpa_select_kernel -- the predicate sdpa_forward itself uses (one shared
  * function, so the query and the launch can never disagree; mlxcel issue
  * #1065 shows an inline copy of such a test drifting from the shared one).
@@ -176,6 +203,11 @@ int sdpa_select_kernel(int batch, int q_len, int kv_len, int n_q_heads, int n_kv
                        int head_dim, sdpa_dtype dtype, sdpa_mask_kind mask_kind,
                        sdpa_kernel* kernel, int* reason);
 
+/* sdpa_select_kernel_ex -- the same predicate with a V head dim (sdpa_forward_ex). */
+int sdpa_select_kernel_ex(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads,
+                          int head_dim, int v_head_dim, sdpa_dtype dtype, sdpa_mask_kind mask_kind,
+                          sdpa_kernel* kernel, int* reason);
+
 /*
  * sdpa_describe_route -- human-readable route for the same arguments: kernel,
  * tile shape, waves, key splits (e.g. "vector bf16 d512 additive splits=64").
@@ -186,6 +218,11 @@ int sdpa_describe_route(int batch, int q_len, int kv_len, int n_q_heads, int n_k
                         int head_dim, sdpa_dtype dtype, sdpa_mask_kind mask_kind,
                         char* buf, size_t len);
 
+/* sdpa_describe_route_ex -- the same with a V head dim (sdpa_forward_ex). */
+int sdpa_describe_route_ex(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads,
+                           int head_dim, int v_head_dim, sdpa_dtype dtype, sdpa_mask_kind mask_kind,
+                           char* buf, size_t len);
+
 /*
  * sdpa_workspace_size -- bytes of workspace sdpa_forward needs for this shape:
  * 0 for the full kernel; for the vector kernel the per-split partial results
@@ -195,6 +232,10 @@ int sdpa_describe_route(int batch, int q_len, int kv_len, int n_q_heads, int n_k
  */
 size_t sdpa_workspace_size(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads,
                            int head_dim, sdpa_dtype dtype);
+
+/* sdpa_workspace_size_ex -- the same with a V head dim (the partial outputs are v_head_dim wide). */
+size_t sdpa_workspace_size_ex(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads,
+                              int head_dim, int v_head_dim, sdpa_dtype dtype);
 
 /* sdpa_head_dims -- writes up to n built head dims (ascending) to out; returns how many exist. */
 int sdpa_head_dims(int* out, int n);

@@ -25,7 +25,9 @@ _TORCH_DT = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: S
              torch.uint8: SDPA_U8, torch.bool: SDPA_U8}
 
 # Every symbol include/sdpa.h declares (checked by the CPU test suite).
-EXPORTS = ("sdpa_forward", "sdpa_forward_sliding", "sdpa_select_kernel", "sdpa_describe_route", "sdpa_workspace_size",
+EXPORTS = ("sdpa_forward", "sdpa_forward_sliding", "sdpa_forward_ex", "sdpa_select_kernel",
+           "sdpa_select_kernel_ex", "sdpa_describe_route", "sdpa_describe_route_ex", "sdpa_workspace_size",
+           "sdpa_workspace_size_ex",
            "sdpa_head_dims", "sdpa_strerror", "sdpa_last_hip_error", "sdpa_route_counters",
            "sdpa_timing_start", "sdpa_timing_stop")
 
@@ -60,13 +62,22 @@ def load(path: str = LIB_PATH):
         lib.sdpa_forward_sliding.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides,
                                              i, i, i, i, i, i, i, ctypes.c_float, i, vp, sz, vp]
         lib.sdpa_forward_sliding.restype = i
+        lib.sdpa_forward_ex.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides,
+                                        i, i, i, i, i, i, i, i, ctypes.c_float, i, vp, Strides, i, i, vp, sz, vp]
+        lib.sdpa_forward_ex.restype = i
         dims = [i, i, i, i, i, i, i]
         lib.sdpa_select_kernel.argtypes = dims + [i, ctypes.POINTER(i), ctypes.POINTER(i)]
         lib.sdpa_select_kernel.restype = i
         lib.sdpa_describe_route.argtypes = dims + [i, ctypes.c_char_p, sz]
         lib.sdpa_describe_route.restype = i
+        lib.sdpa_describe_route_ex.argtypes = dims + [i, i, ctypes.c_char_p, sz]
+        lib.sdpa_describe_route_ex.restype = i
         lib.sdpa_workspace_size.argtypes = dims
         lib.sdpa_workspace_size.restype = sz
+        lib.sdpa_select_kernel_ex.argtypes = dims + [i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+        lib.sdpa_select_kernel_ex.restype = i
+        lib.sdpa_workspace_size_ex.argtypes = dims + [i]
+        lib.sdpa_workspace_size_ex.restype = sz
         lib.sdpa_head_dims.argtypes = [ctypes.POINTER(i), i]
         lib.sdpa_head_dims.restype = i
         lib.sdpa_strerror.argtypes = [i]
@@ -96,23 +107,37 @@ def dtype_code(dt: torch.dtype) -> int:
     return _TORCH_DT[dt]
 
 
-def select_kernel(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind="none"):
+def select_kernel(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind="none",
+                  v_head_dim=None):
     """(kernel name, reason code, status) from the library's routing predicate."""
     k, r = ctypes.c_int(), ctypes.c_int()
-    st = load().sdpa_select_kernel(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
-                                   _as_code(dtype), MASK_KINDS[mask_kind], ctypes.byref(k), ctypes.byref(r))
+    if v_head_dim is None:
+        st = load().sdpa_select_kernel(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
+                                       _as_code(dtype), MASK_KINDS[mask_kind], ctypes.byref(k), ctypes.byref(r))
+    else:
+        st = load().sdpa_select_kernel_ex(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim,
+                                          _as_code(dtype), MASK_KINDS[mask_kind], ctypes.byref(k), ctypes.byref(r))
     return KERNELS[k.value], r.value, st
 
 
-def describe_route(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind="none") -> str:
+def describe_route(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind="none",
+                   v_head_dim=None) -> str:
     buf = ctypes.create_string_buffer(512)
-    load().sdpa_describe_route(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, _as_code(dtype),
-                               MASK_KINDS[mask_kind], buf, len(buf))
+    if v_head_dim is None:
+        load().sdpa_describe_route(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, _as_code(dtype),
+                                   MASK_KINDS[mask_kind], buf, len(buf))
+    else:
+        load().sdpa_describe_route_ex(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim,
+                                      _as_code(dtype), MASK_KINDS[mask_kind], buf, len(buf))
     return buf.value.decode()
 
 
-def workspace_size(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype) -> int:
-    return int(load().sdpa_workspace_size(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, _as_code(dtype)))
+def workspace_size(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, v_head_dim=None) -> int:
+    if v_head_dim is None:
+        return int(load().sdpa_workspace_size(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
+                                              _as_code(dtype)))
+    return int(load().sdpa_workspace_size_ex(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim,
+                                             _as_code(dtype)))
 
 
 def head_dims() -> list:
@@ -189,7 +214,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
             layout: str = "bhld", window: Optional[int] = None) -> torch.Tensor:
     """softmax(scale * q k^T + mask) v on the GPU through libsdpa.so.
 
-    q: [B, Hq, Lq, D], k and v: [B, Hkv, Lk, D] in logical order (any strides,
+    q: [B, Hq, Lq, D], k: [B, Hkv, Lk, D], v: [B, Hkv, Lk, Dv] in logical order (any strides,
     e.g. a transposed view of [B, L, H, D] storage); with layout="blhd" they
     are given in [B, L, H, D] order instead and the result is too.
     mask: broadcastable to [B, Hq, Lq, Lk]; bool/uint8 -> boolean, float ->
@@ -209,7 +234,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
         raise SdpaError(-1, "q, k, v must be 4-D")
     B, Hq, Lq, D = q.shape
     _, Hkv, Lk, _ = k.shape
-    if k.shape[0] != B or k.shape[3] != D or tuple(v.shape) != tuple(k.shape):
+    Dv = v.shape[3]
+    if k.shape[0] != B or k.shape[3] != D or tuple(v.shape[:3]) != tuple(k.shape[:3]):
         raise SdpaError(-1, f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype):
         raise SdpaError(-1, "q, k, v dtypes differ")
@@ -230,14 +256,18 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
             raise SdpaError(-1, "mask must be a device tensor")
         mptr, mst, mdt = mask.data_ptr(), _strides(mask), dtype_code(mask.dtype)
     if out is None:
-        out = torch.empty((B, Hq, Lq, D), dtype=q.dtype, device=q.device)
-    nbytes = lib.sdpa_workspace_size(B, Lq, Lk, Hq, Hkv, D, dt)
+        out = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
+    nbytes = lib.sdpa_workspace_size_ex(B, Lq, Lk, Hq, Hkv, D, Dv, dt)
     if workspace is None:
         workspace = _workspace(nbytes, q.device)
     wptr = workspace.data_ptr() if workspace is not None else None
     wlen = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    if mask_kind == "sliding":
+    if Dv != D:
+        st = lib.sdpa_forward_ex(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
+                                 out.data_ptr(), _strides(out), B, Lq, Lk, Hq, Hkv, D, Dv, dt, float(scale),
+                                 mk, mptr, mst, mdt, int(window or 0), wptr, wlen, stream)
+    elif mask_kind == "sliding":
         if window is None:
             raise SdpaError(-1, "mask_kind=sliding needs window")
         st = lib.sdpa_forward_sliding(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(),

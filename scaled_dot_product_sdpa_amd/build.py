@@ -39,6 +39,12 @@ def head_dims() -> list[int]:
     return [int(x) for x in re.findall(r"X\((\d+)\)", m.group(1))]
 
 
+def head_dim_pairs() -> list[tuple[int, int]]:
+    src = open(os.path.join(CSRC, "launch.h")).read()
+    m = re.search(r"#define SDPA_HEAD_DIM_PAIRS\(X\)(.*)", src)
+    return [(int(a), int(b)) for a, b in re.findall(r"X\((\d+),\s*(\d+)\)", m.group(1))]
+
+
 def _run(cmd):
     t = time.time()
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,10 +58,13 @@ def build(jobs: int | None = None, verbose: bool = True, defines=(), out: str = 
     """Compile every unit and link `out`; `defines` are extra -D flags (tuning experiments)."""
     os.makedirs(build_dir, exist_ok=True)
     tmpl = open(os.path.join(CSRC, "inst_template.hip.in")).read()
+    ptmpl = open(os.path.join(CSRC, "inst_pair_template.hip.in")).read()
+    generated = [(f"inst_d{d}.hip", tmpl.replace("@D@", str(d))) for d in head_dims()]
+    generated += [(f"inst_q{a}_v{b}.hip", ptmpl.replace("@DQ@", str(a)).replace("@DV@", str(b)))
+                  for a, b in head_dim_pairs()]
     units = []
-    for d in head_dims():
-        path = os.path.join(build_dir, f"inst_d{d}.hip")
-        text = tmpl.replace("@D@", str(d))
+    for name, text in generated:
+        path = os.path.join(build_dir, name)
         if not os.path.exists(path) or open(path).read() != text:
             with open(path, "w") as f:
                 f.write(text)

@@ -26,27 +26,29 @@
 
 namespace sdpa_dev {
 
-template <class TR, int D_, int NW_>
+// D: head dim of Q and K; DO: head dim of V and of the output (equal to D
+// except for the (192, 128) pairing of mlx issue #3885, "Current routing").
+template <class TR, int D_, int NW_, int DO_ = D_>
 struct DecCfg {
-    static constexpr int D = D_, NW = NW_, NT = 64 * NW;
+    static constexpr int D = D_, DO = DO_, NW = NW_, NT = 64 * NW;
     static constexpr int KS = 16 * NW;               // keys per chunk
     static constexpr int NCH = (D + 31) / 32;        // Q K^T steps (32 head-dim columns each)
-    static constexpr int DV = (D + 15) / 16 * 16;    // V columns incl. zero pad
+    static constexpr int DV = (DO + 15) / 16 * 16;   // V columns incl. zero pad
     static constexpr int NDB = DV / 16;              // 16-column O^T blocks
     static constexpr int NDBW = (NDB + NW - 1) / NW; // blocks per wave (round robin)
     static constexpr int TP = KS + 4;                // V^T row pitch: 8-byte rows skew, so the 8 rows a
                                                      // transposed store hits at once fall on distinct banks
     static constexpr int PP = KS + 8;                // P row pitch (elements)
-    static constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
+    static constexpr int CPR = DO / 8;               // 16-byte chunks per V row
     static constexpr int VU = (4 * CPR + 63) / 64;   // (4-key, 8-column) V units per lane
     static constexpr int LDS = DV * TP * 2 + 16 * PP * 2 + 2 * NW * 16 * 4;
-    static_assert(D % 8 == 0, "head dim must be a whole number of 16-byte chunks");
+    static_assert(D % 8 == 0 && DO % 8 == 0, "head dims must be whole numbers of 16-byte chunks");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 template <class TR, class C, int MASK>
 __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
-    constexpr int D = C::D, NW = C::NW, KS = C::KS;
+    constexpr int D = C::D, DO = C::DO, NW = C::NW, KS = C::KS;
     constexpr float NEG_INF = -__builtin_inff();
     constexpr bool HAS_MT = (MASK == MASK_ADD16 || MASK == MASK_ADD32 || MASK == MASK_BOOL);
     __shared__ __attribute__((aligned(16))) uint16_t Vt[C::DV * C::TP];
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
     const __amdgpu_buffer_rsrc_t krs =
         make_rsrc(kglob, kend > 0 ? (uint32_t)(kend - 1) * kstep32 + (uint32_t)(D * 2) : 0u);
     const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc(vglob, kend > 0 ? (uint32_t)(kend - 1) * vstep32 + (uint32_t)(D * 2) : 0u);
+        make_rsrc(vglob, kend > 0 ? (uint32_t)(kend - 1) * vstep32 + (uint32_t)(DO * 2) : 0u);
 
     // Q fragments (B operand): row col, head-dim columns 32 i + 8 g .. +7
     u32x4_t qf[C::NCH];
@@ -85,9 +87,9 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
             qf[i] = (rv && d < D) ? *reinterpret_cast<const u32x4_t*>(qrow + d * 2) : u32x4_t{0u, 0u, 0u, 0u};
         }
     }
-    // zero V^T pad rows [D, DV) once (they feed the last O^T block)
-    if constexpr (C::DV > D) {
-        for (int idx = tid; idx < (C::DV - D) * C::TP; idx += C::NT) Vt[D * C::TP + idx] = 0;
+    // zero V^T pad rows [DO, DV) once (they feed the last O^T block)
+    if constexpr (C::DV > DO) {
+        for (int idx = tid; idx < (C::DV - DO) * C::TP; idx += C::NT) Vt[DO * C::TP + idx] = 0;
     }
     const int64_t mrow = HAS_MT ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)qi * p.ms[2] : 0;
     const float c_scale = p.scale_log2;
@@ -217,13 +219,13 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
     // ---- partial state of this split ----
     if (rv) {
         const int64_t row = ((int64_t)b * p.Hq + qh) * p.Lq + qi;
-        float* po = p.ws_o + (row * p.splits + split) * D;
+        float* po = p.ws_o + (row * p.splits + split) * DO;
 #pragma unroll
         for (int i = 0; i < C::NDBW; ++i) {
             const int db = w + NW * i;
             if (db >= C::NDB) break;
             const int d = 16 * db + 4 * g;
-            if (d < D) *reinterpret_cast<f32x4_t*>(po + d) = oacc[i];
+            if (d < DO) *reinterpret_cast<f32x4_t*>(po + d) = oacc[i];
         }
         if (w == 0 && g == 0) {
             p.ws_ml[(row * p.splits + split) * 2 + 0] = m_run;

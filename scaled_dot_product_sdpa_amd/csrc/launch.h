@@ -50,4 +50,12 @@ hipError_t check_launch_once(K kernel, int nt, hipError_t* cache, bool* done) {
 SDPA_HEAD_DIMS(SDPA_DECLARE_GETTER)
 #undef SDPA_DECLARE_GETTER
 
+// (Q/K head dim, V head dim) pairs with built kernels: the vector (decode)
+// kernel only, 16-bit inputs only (null entries elsewhere), as in the routing
+// mlx issue #3885 describes ("Current routing": vector kernel (192, 128)).
+#define SDPA_HEAD_DIM_PAIRS(X) X(192, 128)
+#define SDPA_DECLARE_PAIR_GETTER(DQ, DV) const KernelSet* kernels_q##DQ##_v##DV(int dtype);
+SDPA_HEAD_DIM_PAIRS(SDPA_DECLARE_PAIR_GETTER)
+#undef SDPA_DECLARE_PAIR_GETTER
+
 }  // namespace sdpa_host

@@ -41,17 +41,25 @@ const int kHeadDims[] = {
 #undef SDPA_LIST_D
 };
 
-const KernelSet* kernel_set(sdpa_dtype dt, int d) {
+// Kernels for (Q/K head dim d, V head dim dv); null when none are built.
+const KernelSet* kernel_set(sdpa_dtype dt, int d, int dv) {
     if (dt != SDPA_F32 && dt != SDPA_F16 && dt != SDPA_BF16) return nullptr;
-    switch (d) {
+    if (dv == d) {
+        switch (d) {
 #define SDPA_CASE_D(D) \
     case D:            \
         return sdpa_host::kernels_d##D((int)dt);
-        SDPA_HEAD_DIMS(SDPA_CASE_D)
+            SDPA_HEAD_DIMS(SDPA_CASE_D)
 #undef SDPA_CASE_D
-        default:
-            return nullptr;
+            default:
+                return nullptr;
+        }
     }
+#define SDPA_CASE_PAIR(DQ, DV) \
+    if (d == DQ && dv == DV) return sdpa_host::kernels_q##DQ##_v##DV((int)dt);
+    SDPA_HEAD_DIM_PAIRS(SDPA_CASE_PAIR)
+#undef SDPA_CASE_PAIR
+    return nullptr;
 }
 
 bool head_dim_built(int d) {
@@ -71,12 +79,12 @@ int elem_size(sdpa_dtype dt) {
 }
 
 // The one routing predicate (also behind sdpa_select_kernel).
-int select(int batch, int q_len, int kv_len, int hq, int hkv, int d, sdpa_dtype dt, sdpa_mask_kind mk,
+int select(int batch, int q_len, int kv_len, int hq, int hkv, int d, int dv, sdpa_dtype dt, sdpa_mask_kind mk,
            sdpa_kernel* kernel, int* reason) {
     sdpa_kernel k = SDPA_KERNEL_UNSUPPORTED;
     int why = SDPA_REASON_OK, st = SDPA_OK;
-    if (batch <= 0 || q_len <= 0 || kv_len <= 0 || hq <= 0 || hkv <= 0 || d <= 0 || batch > kMaxGridYZ ||
-        hq > kMaxGridYZ) {
+    if (batch <= 0 || q_len <= 0 || kv_len <= 0 || hq <= 0 || hkv <= 0 || d <= 0 || dv <= 0 ||
+        batch > kMaxGridYZ || hq > kMaxGridYZ) {
         why = SDPA_REASON_SIZE;
         st = SDPA_EINVAL;
     } else if (hq % hkv != 0) {
@@ -88,11 +96,18 @@ int select(int batch, int q_len, int kv_len, int hq, int hkv, int d, sdpa_dtype 
     } else if (dt != SDPA_F32 && dt != SDPA_F16 && dt != SDPA_BF16) {
         why = SDPA_REASON_DTYPE;
         st = SDPA_EUNSUPPORTED;
-    } else if (!head_dim_built(d)) {
+    } else if (dv == d && !head_dim_built(d)) {
         why = SDPA_REASON_HEAD_DIM;
         st = SDPA_EUNSUPPORTED;
     } else {
         k = (q_len <= kVectorMaxQLen) ? SDPA_KERNEL_VECTOR : SDPA_KERNEL_FULL;
+        // a distinct V head dim exists only where a kernel for the pair was built
+        const KernelSet* ks = (dv == d) ? nullptr : kernel_set(dt, d, dv);
+        if (dv != d && (!ks || (k == SDPA_KERNEL_FULL ? !ks->full[0] : !ks->decode[0]))) {
+            k = SDPA_KERNEL_UNSUPPORTED;
+            why = SDPA_REASON_V_HEAD_DIM;
+            st = SDPA_EUNSUPPORTED;
+        }
     }
     if (kernel) *kernel = k;
     if (reason) *reason = why;
@@ -182,28 +197,33 @@ const char* mask_name(sdpa_mask_kind mk) {
     return "?";
 }
 
-std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int d, sdpa_dtype dt,
+std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int d, int dv, sdpa_dtype dt,
                          sdpa_mask_kind mk, int st, sdpa_kernel k, int reason) {
     char buf[256];
+    char dn[32];
+    if (dv == d)
+        std::snprintf(dn, sizeof dn, "%d", d);
+    else
+        std::snprintf(dn, sizeof dn, "%d/v%d", d, dv);
     if (st != SDPA_OK) {
-        std::snprintf(buf, sizeof buf, "unsupported (%s) B=%d Lq=%d Lk=%d Hq=%d Hkv=%d D=%d %s %s: reason %d",
-                      sdpa_strerror(st), batch, q_len, kv_len, hq, hkv, d, dtype_name(dt), mask_name(mk), reason);
+        std::snprintf(buf, sizeof buf, "unsupported (%s) B=%d Lq=%d Lk=%d Hq=%d Hkv=%d D=%s %s %s: reason %d",
+                      sdpa_strerror(st), batch, q_len, kv_len, hq, hkv, dn, dtype_name(dt), mask_name(mk), reason);
         return buf;
     }
-    const KernelSet* ks = kernel_set(dt, d);
+    const KernelSet* ks = kernel_set(dt, d, dv);
     if (k == SDPA_KERNEL_FULL) {
         const auto& t = ks->full_cfg;
         std::snprintf(buf, sizeof buf,
-                      "full %s d%d %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d tile=%dx%d waves=%dx%d lds=%d",
-                      dtype_name(dt), d, mask_name(mk), batch, q_len, kv_len, hq, hkv, t.cols, t.bn, t.wm, t.wd,
+                      "full %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d tile=%dx%d waves=%dx%d lds=%d",
+                      dtype_name(dt), dn, mask_name(mk), batch, q_len, kv_len, hq, hkv, t.cols, t.bn, t.wm, t.wd,
                       t.lds);
     } else {
         const auto& t = ks->dec_cfg;
         DecodePlan p = decode_plan(batch, q_len, kv_len, hq, hkv, t);
         std::snprintf(buf, sizeof buf,
-                      "vector %s d%d %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d splits=%d keys/split=%d colgroups=%d "
+                      "vector %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d splits=%d keys/split=%d colgroups=%d "
                       "cols=%d threads=%d lds=%d",
-                      dtype_name(dt), d, mask_name(mk), batch, q_len, kv_len, hq, hkv, p.splits, p.keys_per_split,
+                      dtype_name(dt), dn, mask_name(mk), batch, q_len, kv_len, hq, hkv, p.splits, p.keys_per_split,
                       p.col_groups, t.cols, t.nt, t.lds);
     }
     return buf;
@@ -250,32 +270,51 @@ extern "C" {
 
 int sdpa_select_kernel(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
                        sdpa_dtype dtype, sdpa_mask_kind mask_kind, sdpa_kernel* kernel, int* reason) {
-    return select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, kernel, reason);
+    return select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, head_dim, dtype, mask_kind, kernel, reason);
 }
 
-int sdpa_describe_route(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
-                        sdpa_dtype dtype, sdpa_mask_kind mask_kind, char* buf, size_t len) {
+int sdpa_select_kernel_ex(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
+                          int v_head_dim, sdpa_dtype dtype, sdpa_mask_kind mask_kind, sdpa_kernel* kernel,
+                          int* reason) {
+    return select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype, mask_kind, kernel,
+                  reason);
+}
+
+int sdpa_describe_route_ex(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
+                           int v_head_dim, sdpa_dtype dtype, sdpa_mask_kind mask_kind, char* buf, size_t len) {
     sdpa_kernel k;
     int reason;
-    const int st = select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, &k, &reason);
+    const int st =
+        select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype, mask_kind, &k, &reason);
     if (buf && len) {
-        const std::string s =
-            route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, st, k, reason);
+        const std::string s = route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
+                                           mask_kind, st, k, reason);
         std::snprintf(buf, len, "%s", s.c_str());
     }
     return st;
 }
 
-size_t sdpa_workspace_size(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
-                           sdpa_dtype dtype) {
+int sdpa_describe_route(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
+                        sdpa_dtype dtype, sdpa_mask_kind mask_kind, char* buf, size_t len) {
+    return sdpa_describe_route_ex(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, head_dim, dtype, mask_kind,
+                                  buf, len);
+}
+
+size_t sdpa_workspace_size_ex(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
+                              int v_head_dim, sdpa_dtype dtype) {
     sdpa_kernel k;
-    if (select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, SDPA_MASK_NONE, &k, nullptr) !=
-            SDPA_OK ||
+    if (select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype, SDPA_MASK_NONE, &k,
+               nullptr) != SDPA_OK ||
         k != SDPA_KERNEL_VECTOR)
         return 0;
-    const KernelSet* ks = kernel_set(dtype, head_dim);
+    const KernelSet* ks = kernel_set(dtype, head_dim, v_head_dim);
     const DecodePlan p = decode_plan(batch, q_len, kv_len, n_q_heads, n_kv_heads, ks->dec_cfg);
-    return decode_ws_bytes(batch, q_len, n_q_heads, head_dim, p);
+    return decode_ws_bytes(batch, q_len, n_q_heads, v_head_dim, p);
+}
+
+size_t sdpa_workspace_size(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
+                           sdpa_dtype dtype) {
+    return sdpa_workspace_size_ex(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, head_dim, dtype);
 }
 
 int sdpa_head_dims(int* out, int n) {
@@ -347,31 +386,34 @@ namespace {
 
 int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
                  sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len, int n_q_heads,
-                 int n_kv_heads, int head_dim, sdpa_dtype dtype, float scale, sdpa_mask_kind mask_kind,
+                 int n_kv_heads, int head_dim, int v_head_dim, sdpa_dtype dtype, float scale, sdpa_mask_kind mask_kind,
                  const void* mask, sdpa_strides mask_st, sdpa_dtype mask_dtype, int window, void* workspace,
                  size_t workspace_bytes, void* stream) {
     sdpa_kernel kern;
     int reason;
-    int st = select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, &kern, &reason);
+    int st = select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype, mask_kind, &kern,
+                    &reason);
     if (st != SDPA_OK) return reject(st);
     if (!std::isfinite(scale)) return reject(SDPA_EINVAL);
 
     const int es = elem_size(dtype);
     const int64_t nq[4] = {batch, n_q_heads, q_len, head_dim};
     const int64_t nk[4] = {batch, n_kv_heads, kv_len, head_dim};
+    const int64_t nv[4] = {batch, n_kv_heads, kv_len, v_head_dim};
+    const int64_t no[4] = {batch, n_q_heads, q_len, v_head_dim};
     if ((st = check_operand(q, q_st, nq, es)) != SDPA_OK) return reject(st);
     if ((st = check_operand(k, k_st, nk, es)) != SDPA_OK) return reject(st);
-    if ((st = check_operand(v, v_st, nk, es)) != SDPA_OK) return reject(st);
-    if ((st = check_operand(out, o_st, nq, es)) != SDPA_OK) return reject(st);
+    if ((st = check_operand(v, v_st, nv, es)) != SDPA_OK) return reject(st);
+    if ((st = check_operand(out, o_st, no, es)) != SDPA_OK) return reject(st);
     // K/V rows are read through 32-bit buffer offsets from each (batch, kv head)
     // base: rows may not overlap and one head's keys must span < 4 GiB.
-    if (kv_len > 1 && (k_st.l < head_dim || v_st.l < head_dim)) return reject(SDPA_EUNSUPPORTED);
+    if (kv_len > 1 && (k_st.l < head_dim || v_st.l < v_head_dim)) return reject(SDPA_EUNSUPPORTED);
     if ((double)kv_len * (double)(k_st.l > 0 ? k_st.l : 1) * es >= 4294967296.0 ||
         (double)kv_len * (double)(v_st.l > 0 ? v_st.l : 1) * es >= 4294967296.0)
         return reject(SDPA_EUNSUPPORTED);
-    const size_t oq = span_bytes(nq, o_st, es);
+    const size_t oq = span_bytes(no, o_st, es);
     if (overlaps(out, oq, q, span_bytes(nq, q_st, es)) || overlaps(out, oq, k, span_bytes(nk, k_st, es)) ||
-        overlaps(out, oq, v, span_bytes(nk, v_st, es)))
+        overlaps(out, oq, v, span_bytes(nv, v_st, es)))
         return reject(SDPA_EINVAL);
 
     Params p{};
@@ -419,7 +461,7 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     p.window = window;
     p.kbase = 0;
 
-    const KernelSet* ks = kernel_set(dtype, head_dim);
+    const KernelSet* ks = kernel_set(dtype, head_dim, v_head_dim);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // kernel mask variant: the additive kind splits by mask element width
     int mk = (int)mask_kind;
@@ -451,8 +493,8 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         const long items = (long)((q_len + bm - 1) / bm) * (n_q_heads / hg) * batch;
         if (items > (1L << 30)) return reject(SDPA_EUNSUPPORTED);
         dim3 grid((unsigned)(8 * ((items + 7) / 8)), 1, 1);
-        log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, st,
-                                    kern, reason));
+        log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
+                                    mask_kind, st, kern, reason));
         mark(0);
         st = hip_status(ks->full[mk](p, grid, s));
         if (st != SDPA_OK) return reject(st);
@@ -470,7 +512,7 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         p.kbase = lo > 0 ? (int)lo : 0;
     }
     const DecodePlan plan = decode_plan(batch, q_len, kv_len - p.kbase, n_q_heads, n_kv_heads, t);
-    const size_t need = decode_ws_bytes(batch, q_len, n_q_heads, head_dim, plan);
+    const size_t need = decode_ws_bytes(batch, q_len, n_q_heads, v_head_dim, plan);
     if (!workspace || workspace_bytes < need) return reject(SDPA_EWORKSPACE);
     if (((uintptr_t)workspace) % 256 != 0) return reject(SDPA_EINVAL);
     if (overlaps(out, oq, workspace, need)) return reject(SDPA_EINVAL);
@@ -478,18 +520,18 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     const size_t rows = (size_t)batch * n_q_heads * q_len;
     p.ws_o = reinterpret_cast<float*>(workspace);
     p.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                       align256(rows * plan.splits * head_dim * sizeof(float)));
+                                       align256(rows * plan.splits * v_head_dim * sizeof(float)));
     p.splits = plan.splits;
     p.keys_per_split = plan.keys_per_split;
     p.col_groups = plan.col_groups;
-    log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind, st, kern,
-                                reason));
+    log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype, mask_kind,
+                                st, kern, reason));
     dim3 grid((unsigned)plan.splits, (unsigned)(n_kv_heads * plan.col_groups), (unsigned)batch);
     mark(0);
     st = hip_status(ks->decode[mk](p, grid, s));
     if (st != SDPA_OK) return reject(st);
     mark(1);
-    dim3 cgrid((unsigned)rows, (unsigned)((head_dim + 63) / 64), 1);
+    dim3 cgrid((unsigned)rows, (unsigned)((v_head_dim + 63) / 64), 1);
     st = hip_status(ks->combine(p, cgrid, s));
     if (st != SDPA_OK) return reject(st);
     mark(2);
@@ -507,7 +549,8 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     g_counters[0].fetch_add(1, std::memory_order_relaxed);
     if (mask_kind == SDPA_MASK_SLIDING) return reject(SDPA_EINVAL);  // needs a window: sdpa_forward_sliding
     return forward_impl(q, q_st, k, k_st, v, v_st, out, o_st, batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
-                        dtype, scale, mask_kind, mask, mask_st, mask_dtype, 0, workspace, workspace_bytes, stream);
+                        head_dim, dtype, scale, mask_kind, mask, mask_st, mask_dtype, 0, workspace, workspace_bytes,
+                        stream);
 }
 
 int sdpa_forward_sliding(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
@@ -518,8 +561,20 @@ int sdpa_forward_sliding(const void* q, sdpa_strides q_st, const void* k, sdpa_s
     if (window < 1) return reject(SDPA_EINVAL);
     const sdpa_strides none{0, 0, 0, 0};
     return forward_impl(q, q_st, k, k_st, v, v_st, out, o_st, batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
-                        dtype, scale, SDPA_MASK_SLIDING, nullptr, none, SDPA_F32, window, workspace, workspace_bytes,
-                        stream);
+                        head_dim, dtype, scale, SDPA_MASK_SLIDING, nullptr, none, SDPA_F32, window, workspace,
+                        workspace_bytes, stream);
+}
+
+int sdpa_forward_ex(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
+                    sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len, int n_q_heads,
+                    int n_kv_heads, int head_dim, int v_head_dim, sdpa_dtype dtype, float scale,
+                    sdpa_mask_kind mask_kind, const void* mask, sdpa_strides mask_st, sdpa_dtype mask_dtype, int window,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    g_counters[0].fetch_add(1, std::memory_order_relaxed);
+    if (mask_kind == SDPA_MASK_SLIDING && window < 1) return reject(SDPA_EINVAL);
+    return forward_impl(q, q_st, k, k_st, v, v_st, out, o_st, batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
+                        v_head_dim, dtype, scale, mask_kind, mask, mask_st, mask_dtype,
+                        mask_kind == SDPA_MASK_SLIDING ? window : 0, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

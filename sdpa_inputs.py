@@ -79,8 +79,10 @@ def linspace_block(shape) -> np.ndarray:
 
 def make_case(B, Hq, Hkv, Lq, Lk, D, dtype="bf16", layout="bhld", mask_kind="none",
               seed=0, std=1.0, scale=None, mask_p=None, mask_shape="key",
-              mask_dtype=None, name="", window=None) -> Case:
+              mask_dtype=None, name="", window=None, dv=None) -> Case:
     """Seeded random case.
+
+    dv: head dim of V (and of the output) when it differs from D.
 
     window: keys per query for mask_kind="sliding" (kept in meta["window"]).
 
@@ -92,8 +94,8 @@ def make_case(B, Hq, Hkv, Lq, Lk, D, dtype="bf16", layout="bhld", mask_kind="non
     tdt = DTYPES[dtype]
     g = rng(seed)
     tensors = []
-    for H, L in ((Hq, Lq), (Hkv, Lk), (Hkv, Lk)):
-        x = g.standard_normal(_phys_shape(B, H, L, D, layout), dtype=np.float32) * np.float32(std)
+    for H, L, DD in ((Hq, Lq, D), (Hkv, Lk, D), (Hkv, Lk, dv or D)):
+        x = g.standard_normal(_phys_shape(B, H, L, DD, layout), dtype=np.float32) * np.float32(std)
         tensors.append(logical_view(torch.from_numpy(x).to(tdt), layout))
     q, k, v = tensors
     if scale is None:
@@ -171,6 +173,14 @@ def sliding_case(q_len=4096, kv_len=4096, window=1024, dtype="bf16") -> Case:
     [B,H,L,D]; q_len=1 is a decode step over a kv_len cache (seed 6)."""
     return make_case(1, 32, 16, q_len, kv_len, 256, dtype=dtype, layout="bhld", mask_kind="sliding",
                      seed=6, window=window, name=f"sliding-d256-q{q_len}-k{kv_len}-w{window}")
+
+
+def decode_dv_case(kv_len=4096, dtype="bf16") -> Case:
+    """bf16 decode with the (192, 128) head-dim pairing of the vector kernel in
+    mlx issue #3885 [Current routing]: B=1, qL=1, Hq=32, Hkv=8, Q/K head dim 192,
+    V head dim 128, additive [1,1,1,Lk] mask (10% -1e9), [B,H,L,D] (seed 7)."""
+    return make_case(1, 32, 8, 1, kv_len, 192, dtype=dtype, layout="bhld", mask_kind="additive", seed=7,
+                     dv=128, name=f"decode-qk192-v128-lk{kv_len}")
 
 
 def to_device(case: Case, device="cuda"):

@@ -66,6 +66,24 @@ def test_every_dtype_and_head_dim_is_fused(lib):
                 assert sdpa.select_kernel(2, 1, 100, 8, 2, d, dt, mk)[0] == "vector"
 
 
+def test_value_head_dim_pairing(lib):
+    """(192, 128) exists for the 16-bit vector kernel only; other pairings are
+    unsupported with their own reason (6)."""
+    for dt in (1, 2):
+        assert sdpa.select_kernel(1, 1, 4096, 32, 8, 192, dt, "additive", v_head_dim=128) == ("vector", 0, 0)
+        assert sdpa.select_kernel(1, 8, 4096, 32, 8, 192, dt, "sliding", v_head_dim=128) == ("vector", 0, 0)
+        assert sdpa.select_kernel(1, 9, 4096, 32, 8, 192, dt, "none", v_head_dim=128) == ("unsupported", 6, -2)
+    assert sdpa.select_kernel(1, 1, 4096, 32, 8, 192, 0, "none", v_head_dim=128) == ("unsupported", 6, -2)
+    assert sdpa.select_kernel(1, 1, 4096, 32, 8, 128, 2, "none", v_head_dim=64) == ("unsupported", 6, -2)
+    assert sdpa.select_kernel(1, 1, 4096, 32, 8, 192, 2, "none") == ("unsupported", 1, -2)
+    assert sdpa.select_kernel(1, 1, 4096, 32, 8, 128, 2, "none", v_head_dim=128) == ("vector", 0, 0)
+    # partial outputs are v_head_dim wide: same plan, 128 / 192 of the fp32 outputs
+    a = sdpa.workspace_size(1, 1, 4096, 32, 8, 128, 2)
+    b = sdpa.workspace_size(1, 1, 4096, 32, 8, 192, 2, v_head_dim=128)
+    assert a == b > 0
+    assert sdpa.workspace_size(1, 9, 4096, 32, 8, 192, 2, v_head_dim=128) == 0
+
+
 def test_describe_route(lib):
     s = sdpa.describe_route(1, 1, 4096, 32, 4, 512, 2, "additive")
     assert s.startswith("vector bf16 d512 additive") and "splits=" in s

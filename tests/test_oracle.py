@@ -259,6 +259,21 @@ def test_sliding_window_chunks_match_the_block():
         np.testing.assert_allclose(part, full[:, :, s0:s1], rtol=1e-13, atol=1e-14)
 
 
+def test_value_head_dim_columns_are_independent():
+    """O's columns depend only on the matching V columns: a V head dim of 128
+    under 192-wide queries and keys is the first 128 columns of the 192-wide
+    result (the (192, 128) pairing); brute force agrees."""
+    q, k, v = _rand((1, 4, 5, 192), 1), _rand((1, 2, 9, 192), 2), _rand((1, 2, 9, 192), 3)
+    for kind, m in (("none", None), ("causal", None), ("sliding", 3)):
+        wide = oracle.sdpa(q, k, v, 0.07, kind, m)
+        narrow = oracle.sdpa(q, k, v[..., :128], 0.07, kind, m)
+        assert narrow.shape == (1, 4, 5, 128)
+        np.testing.assert_array_equal(narrow, wide[..., :128])
+    small = (q[:, :, :3, :6], k[:, :, :4, :6], v[:, :, :4, :2])
+    np.testing.assert_allclose(oracle.sdpa(*small, 0.3, "causal"), oracle.brute_force_sdpa(*small, 0.3, "causal"),
+                               rtol=1e-13, atol=1e-14)
+
+
 def test_constant_additive_shift_is_invariant():
     q, k, v = _rand((1, 2, 6, 4), 1), _rand((1, 2, 9, 4), 2), _rand((1, 2, 9, 4), 3)
     m = _rand((1, 1, 6, 9), 4)

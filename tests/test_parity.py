@@ -168,3 +168,19 @@ def test_prefill_sliding_window_wide_groups(gpu_lib, D, hq, hkv):
     c = si.make_case(1, hq, hkv, 150, 150, D, dtype="bf16", layout="bhld", mask_kind="sliding",
                      seed=D + hq, window=45)
     assert_parity(run_gpu(c), oracle_out(c), "bf16", f"prefill sliding D={D} Hq={hq} Hkv={hkv}")
+
+
+# --------------------------------------------------------------------------
+# Distinct V head dim: the (192, 128) pairing of the vector kernel, every
+# mask kind, one and several query rows per head, GQA.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("lk", [300, 4100])
+@pytest.mark.parametrize("lq", [1, 5])
+@pytest.mark.parametrize("mask_kind", MASKS + ["sliding"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_decode_qk192_v128(gpu_lib, dtype, mask_kind, lq, lk):
+    c = si.make_case(1, 16, 4, lq, lk, 192, dtype=dtype, layout="bhld", mask_kind=mask_kind, seed=lk + lq,
+                     mask_shape="qk", mask_p=0.2, dv=128, window=100 if mask_kind == "sliding" else None)
+    out = run_gpu(c)
+    assert tuple(out.shape) == (1, 16, lq, 128)
+    assert_parity(out, oracle_out(c), dtype, f"decode qk192/v128 {dtype} {mask_kind} Lq={lq} Lk={lk}")
