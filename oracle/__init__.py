@@ -7,6 +7,8 @@ from .sdpa_oracle import (  # noqa: F401
     mask_bias,
     merge_states,
     partial_state,
+    rope,
+    rope_tables,
     sdpa,
     sdpa_strided,
 )

@@ -36,6 +36,12 @@ Readings where the pages are silent (each is also listed in the design notes):
     i + (Lk - Lq), and attends to keys j <= that position;
   * an additive mask is added after the scale (it is not scaled);
   * a row whose every key is masked has no defined softmax; its output is 0;
+  * rotary position embedding (RoPE) follows the rotate-half convention of
+    the pre-computed cos/sin tables named in mlx issue #3585 [Model config]
+    ([positions, head_dim] tables, base 10000): the first R head-dim columns
+    form pairs (c, c + R/2) rotated by the angle of (position, c); columns
+    >= R pass through ("25% partial RoPE" in mlx issue #3885 [Summary] is
+    R = D/4).  The tables are inputs: cos[pos][c], sin[pos][c], c < R/2;
   * sliding (local) attention keeps the causal alignment and a window of W
     keys: query i at position pos = i + (Lk - Lq) attends keys j with
     pos - W < j <= pos (the page names the layer type, not its formula; this
@@ -195,6 +201,45 @@ def sdpa_strided(q_flat, q_strides, k_flat, k_strides, v_flat, v_strides,
     k = gather_strided(k_flat, (batch, n_kv_heads, kv_len, head_dim), k_strides)
     v = gather_strided(v_flat, (batch, n_kv_heads, kv_len, head_dim), v_strides)
     return sdpa(q, k, v, scale, mask_kind, mask)
+
+
+# --------------------------------------------------------------------------
+# Rotary position embedding (applied to Q and K before the scores).
+# --------------------------------------------------------------------------
+def rope(x, cos, sin, rotary_dim: int, pos0: int = 0) -> np.ndarray:
+    """Rotate the first rotary_dim columns of x (logical [..., L, D]) in pairs.
+
+    Row l sits at position pos0 + l.  With R = rotary_dim, h = R / 2 and
+    (c, s) = (cos[pos][j], sin[pos][j]) for j < h:
+        y[j]     = x[j] * c - x[j + h] * s
+        y[j + h] = x[j + h] * c + x[j] * s
+    and y[j] = x[j] for j >= R.  float64 throughout.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    R = int(rotary_dim)
+    if R == 0:
+        return x.copy()
+    if R < 0 or R % 2 or R > x.shape[-1]:
+        raise ValueError("rotary_dim must be even and at most the head dim")
+    h = R // 2
+    L = x.shape[-2]
+    c = np.asarray(cos, dtype=np.float64)[pos0:pos0 + L, :h]
+    s = np.asarray(sin, dtype=np.float64)[pos0:pos0 + L, :h]
+    if c.shape[0] != L:
+        raise ValueError("the tables do not cover every position")
+    y = x.copy()
+    a, b = x[..., :h], x[..., h:R]
+    y[..., :h] = a * c - b * s
+    y[..., h:R] = b * c + a * s
+    return y
+
+
+def rope_tables(n_pos: int, rotary_dim: int, base: float = 10000.0):
+    """The usual tables: angle(pos, j) = pos * base ** (-2 j / R), j < R / 2."""
+    h = rotary_dim // 2
+    inv = base ** (-2.0 * np.arange(h, dtype=np.float64) / rotary_dim)
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang), np.sin(ang)
 
 
 # --------------------------------------------------------------------------

@@ -274,6 +274,36 @@ def test_value_head_dim_columns_are_independent():
                                rtol=1e-13, atol=1e-14)
 
 
+def test_rope_scores_depend_only_on_relative_position():
+    """With the usual tables, <RoPE(q) at i, RoPE(k) at j> depends on i - j only."""
+    cos, sin = oracle.rope_tables(64, 32)
+    q, k = _rand((1, 1, 1, 48), 1), _rand((1, 1, 1, 48), 2)
+    def dot(i, j):
+        return float((oracle.rope(q, cos, sin, 32, i) * oracle.rope(k, cos, sin, 32, j)).sum())
+    for i, j, shift in ((5, 2, 7), (0, 9, 30), (20, 20, 11)):
+        assert abs(dot(i, j) - dot(i + shift, j + shift)) < 1e-12
+    assert abs(dot(5, 2) - dot(2, 5)) > 1e-3  # but the sign of i - j matters
+
+
+def test_rope_closed_forms():
+    x = _rand((2, 3, 4, 16), 3)
+    cos, sin = oracle.rope_tables(8, 8)
+    y = oracle.rope(x, cos, sin, 8, 2)
+    np.testing.assert_array_equal(y[..., 8:], x[..., 8:])                  # columns >= R pass through
+    np.testing.assert_array_equal(oracle.rope(x, cos, sin, 0), x)          # R = 0: identity
+    np.testing.assert_allclose(oracle.rope(x[..., :1, :], cos, sin, 8, 0), x[..., :1, :], atol=0)  # position 0
+    pair = x[..., :4] ** 2 + x[..., 4:8] ** 2                              # each (j, j + R/2) pair keeps its norm
+    np.testing.assert_allclose(y[..., :4] ** 2 + y[..., 4:8] ** 2, pair, rtol=1e-13)
+    np.testing.assert_allclose(oracle.rope(y, cos, -sin, 8, 2), x, rtol=1e-13, atol=1e-14)  # inverse rotation
+    # a quarter turn maps (a, b) to (-b, a)
+    qc, qs = np.zeros((1, 1)), np.ones((1, 1))
+    v = np.array([[[[3.0, 5.0]]]])
+    np.testing.assert_array_equal(oracle.rope(v, qc, qs, 2, 0), np.array([[[[-5.0, 3.0]]]]))
+    # the tables are the angle pos * 10000^(-2j/R)
+    c, s_ = oracle.rope_tables(5, 6)
+    assert abs(c[3, 2] - math.cos(3 * 10000 ** (-4 / 6))) < 1e-15 and abs(s_[4, 1] - math.sin(4 * 10000 ** (-2 / 6))) < 1e-15
+
+
 def test_constant_additive_shift_is_invariant():
     q, k, v = _rand((1, 2, 6, 4), 1), _rand((1, 2, 9, 4), 2), _rand((1, 2, 9, 4), 3)
     m = _rand((1, 1, 6, 9), 4)
@@ -328,7 +358,8 @@ def _pins_hold():
             test_gqa_equals_mha_with_repeated_kv,
             test_identical_keys_give_mean_of_v_and_causal_prefix_means,
             test_one_hot_scores_do_not_overflow,
-            test_sliding_window_closed_forms]
+            test_sliding_window_closed_forms,
+            test_rope_closed_forms]
     pins += [lambda k=k: test_oracle_matches_torch_float64(k) for k in oracle.MASK_KINDS]
     pins += [lambda k=k: test_oracle_matches_brute_force(k, 3, 5) for k in oracle.MASK_KINDS]
     with np.errstate(all="ignore"):
@@ -346,7 +377,8 @@ def test_pins_hold_for_the_real_oracle():
 
 @pytest.mark.parametrize("mutation", ["no_scale", "softmax_over_queries", "reversed_v_rows",
                                       "head_modulo", "causal_top_left", "mask_dropped",
-                                      "mask_scaled", "no_max_shift", "sliding_window_plus_one"])
+                                      "mask_scaled", "no_max_shift", "sliding_window_plus_one",
+                                      "rope_sign_flip", "rope_adjacent_pairs"])
 def test_planted_mistakes_are_caught(monkeypatch, mutation):
     """Plant a plausible mistake in the oracle (CPU) and check that a pin fails."""
     if mutation == "no_scale":
@@ -382,6 +414,25 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
                             orig("none", None, lq, lk) if kind == "additive" else orig(kind, mask, lq, lk))
     elif mutation == "mask_scaled":
         monkeypatch.setattr(so, "_scores", lambda qh, kg, scale, b: (qh @ kg.T + b) * float(scale))
+    elif mutation == "rope_sign_flip":
+        orig = so.rope
+
+        def bad(x, cos, sin, r, pos0=0):
+            return orig(x, cos, -np.asarray(sin), r, pos0)
+        monkeypatch.setattr(so, "rope", bad)
+        monkeypatch.setattr(oracle, "rope", bad)
+    elif mutation == "rope_adjacent_pairs":   # the interleaved (2j, 2j+1) convention instead of (j, j + R/2)
+        orig = so.rope
+
+        def bad(x, cos, sin, r, pos0=0):
+            x = np.asarray(x, dtype=np.float64)
+            if r == 0:
+                return x.copy()
+            idx = np.concatenate([np.arange(0, r, 2), np.arange(1, r, 2), np.arange(r, x.shape[-1])])
+            inv = np.argsort(idx)
+            return orig(x[..., idx], cos, sin, r, pos0)[..., inv]
+        monkeypatch.setattr(so, "rope", bad)
+        monkeypatch.setattr(oracle, "rope", bad)
     elif mutation == "sliding_window_plus_one":
         orig = so.mask_bias
         monkeypatch.setattr(so, "mask_bias", lambda kind, mask, lq, lk:
