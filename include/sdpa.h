@@ -96,6 +96,22 @@ typedef struct {
     int64_t b, h, l, d;
 } sdpa_strides;
 
+/* Rotary position embedding tables (rotate-half convention of the
+ * pre-computed cos/sin tables in mlx issue #3585, "Model config"; partial
+ * rotation as the "25% partial RoPE" layers of mlx issue #3885, "Summary").
+ * A row at position pos has its head-dim columns j and j + R/2 (j < R/2)
+ * turned by the angle of (pos, j):
+ *     y[j]       = x[j] cos[pos][j] - x[j + R/2] sin[pos][j]
+ *     y[j + R/2] = x[j + R/2] cos[pos][j] + x[j] sin[pos][j]
+ * columns >= R are unchanged.  Computed in fp32, rounded once to the element
+ * type.  cos and sin are device float32 [n_pos][R/2] row-major, 16-byte aligned. */
+typedef struct {
+    int rotary_dim;   /* R: even; 0 = no rotation                      */
+    const float* cos; /* [n_pos][R / 2]                                  */
+    const float* sin; /* [n_pos][R / 2]                                  */
+    int n_pos;        /* table rows; every position used must be < n_pos */
+} sdpa_rope_table;
+
 /* Status codes. */
 #define SDPA_OK 0
 #define SDPA_EINVAL (-1)       /* null pointer, non-positive size, Hq % Hkv != 0, bad mask args */
@@ -177,6 +193,14 @@ int sdpa_forward_sliding(const void* q, sdpa_strides q_st,
  *                  reason SDPA_REASON_V_HEAD_DIM.
  *   window         keys per query when mask_kind is SDPA_MASK_SLIDING (>= 1,
  *                  else SDPA_EINVAL); ignored for the other kinds.
+ *   q_rope, q_pos0 rotary embedding of Q inside the attention kernels (NULL or
+ *                  rotary_dim 0: none).  Query row i sits at position q_pos0 + i
+ *                  (q_pos0 = kv_len - q_len continues the keys).  K is taken as
+ *                  already rotated: rotate keys once with sdpa_rope when they
+ *                  are written (a cache keeps rotated keys), not on every call.
+ *                  Needs dtype F16 or BF16, rotary_dim a multiple of 64 and at
+ *                  most head_dim, and 0 <= q_pos0, q_pos0 + q_len <= n_pos
+ *                  (SDPA_EUNSUPPORTED / SDPA_EINVAL otherwise).
  * Everything else as sdpa_forward; the workspace is sdpa_workspace_size_ex().
  */
 int sdpa_forward_ex(const void* q, sdpa_strides q_st,
@@ -188,8 +212,21 @@ int sdpa_forward_ex(const void* q, sdpa_strides q_st,
                     sdpa_dtype dtype, float scale,
                     sdpa_mask_kind mask_kind, const void* mask, sdpa_strides mask_st,
                     sdpa_dtype mask_dtype, int window,
+                    const sdpa_rope_table* q_rope, int q_pos0,
                     void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * sdpa_rope -- y = the rotary embedding of x (see sdpa_rope_table): row l of
+ * every (batch, head) sits at position pos0 + l.  x and y are device
+ * [batch, n_heads, len, head_dim] tensors of `dtype` (F32, F16, BF16) with
+ * logical strides (d stride 1); y may be x (in place) but may not otherwise
+ * overlap it.  rotary_dim: even, 2 .. head_dim.  0 <= pos0, pos0 + len <= n_pos.
+ * HBM-bound elementwise kernel on `stream`; returns SDPA_OK or a status.
+ */
+int sdpa_rope(const void* x, sdpa_strides x_st, void* y, sdpa_strides y_st,
+              int batch, int n_heads, int len, int head_dim, sdpa_dtype dtype,
+              const sdpa_rope_table* rope, int pos0, void* stream);
 
 /*
  * sdpa_select_kernel -- the predicate sdpa_forward itself uses (one shared

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     head_dims,
     kernel_timing,
     load,
+    rope,
     route_counters,
     select_kernel,
     workspace_size,

@@ -25,7 +25,7 @@ _TORCH_DT = {torch.float32: SDPA_F32, torch.float16: SDPA_F16, torch.bfloat16: S
              torch.uint8: SDPA_U8, torch.bool: SDPA_U8}
 
 # Every symbol include/sdpa.h declares (checked by the CPU test suite).
-EXPORTS = ("sdpa_forward", "sdpa_forward_sliding", "sdpa_forward_ex", "sdpa_select_kernel",
+EXPORTS = ("sdpa_forward", "sdpa_forward_sliding", "sdpa_forward_ex", "sdpa_rope", "sdpa_select_kernel",
            "sdpa_select_kernel_ex", "sdpa_describe_route", "sdpa_describe_route_ex", "sdpa_workspace_size",
            "sdpa_workspace_size_ex",
            "sdpa_head_dims", "sdpa_strerror", "sdpa_last_hip_error", "sdpa_route_counters",
@@ -34,6 +34,11 @@ EXPORTS = ("sdpa_forward", "sdpa_forward_sliding", "sdpa_forward_ex", "sdpa_sele
 
 class Strides(ctypes.Structure):
     _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("l", ctypes.c_int64), ("d", ctypes.c_int64)]
+
+
+class RopeTable(ctypes.Structure):
+    _fields_ = [("rotary_dim", ctypes.c_int), ("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p),
+                ("n_pos", ctypes.c_int)]
 
 
 class SdpaError(RuntimeError):
@@ -63,7 +68,10 @@ def load(path: str = LIB_PATH):
                                              i, i, i, i, i, i, i, ctypes.c_float, i, vp, sz, vp]
         lib.sdpa_forward_sliding.restype = i
         lib.sdpa_forward_ex.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides,
-                                        i, i, i, i, i, i, i, i, ctypes.c_float, i, vp, Strides, i, i, vp, sz, vp]
+                                        i, i, i, i, i, i, i, i, ctypes.c_float, i, vp, Strides, i, i,
+                                        ctypes.POINTER(RopeTable), i, vp, sz, vp]
+        lib.sdpa_rope.argtypes = [vp, Strides, vp, Strides, i, i, i, i, i, ctypes.POINTER(RopeTable), i, vp]
+        lib.sdpa_rope.restype = i
         lib.sdpa_forward_ex.restype = i
         dims = [i, i, i, i, i, i, i]
         lib.sdpa_select_kernel.argtypes = dims + [i, ctypes.POINTER(i), ctypes.POINTER(i)]
@@ -211,7 +219,8 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
             mask: Optional[torch.Tensor] = None, mask_kind: Optional[str] = None,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-            layout: str = "bhld", window: Optional[int] = None) -> torch.Tensor:
+            layout: str = "bhld", window: Optional[int] = None, rope=None,
+            q_pos0: Optional[int] = None) -> torch.Tensor:
     """softmax(scale * q k^T + mask) v on the GPU through libsdpa.so.
 
     q: [B, Hq, Lq, D], k: [B, Hkv, Lk, D], v: [B, Hkv, Lk, Dv] in logical order (any strides,
@@ -220,6 +229,9 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
     mask: broadcastable to [B, Hq, Lq, Lk]; bool/uint8 -> boolean, float ->
     additive; mask_kind="causal" needs no tensor; mask_kind="sliding" takes
     `window` (the number of most recent keys each query attends, >= 1).
+    rope: (cos, sin, rotary_dim) rotates Q inside the kernels (K must already
+    be rotated, e.g. by rope() below); query row i sits at position
+    q_pos0 + i, q_pos0 defaulting to Lk - Lq.
     """
     lib = load()
     if layout == "blhd":
@@ -263,10 +275,16 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
     wptr = workspace.data_ptr() if workspace is not None else None
     wlen = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    if Dv != D:
+    if Dv != D or rope is not None:
+        table = None
+        if rope is not None:
+            table = _rope_table(*rope, device=q.device)
+        if q_pos0 is None:
+            q_pos0 = Lk - Lq
         st = lib.sdpa_forward_ex(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(), _strides(v),
                                  out.data_ptr(), _strides(out), B, Lq, Lk, Hq, Hkv, D, Dv, dt, float(scale),
-                                 mk, mptr, mst, mdt, int(window or 0), wptr, wlen, stream)
+                                 mk, mptr, mst, mdt, int(window or 0),
+                                 ctypes.byref(table) if table is not None else None, int(q_pos0), wptr, wlen, stream)
     elif mask_kind == "sliding":
         if window is None:
             raise SdpaError(-1, "mask_kind=sliding needs window")
@@ -280,4 +298,39 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
     if st != 0:
         raise SdpaError(st, f"sdpa_forward(B={B}, Lq={Lq}, Lk={Lk}, Hq={Hq}, Hkv={Hkv}, D={D}, {q.dtype}, "
                             f"{mask_kind})")
+    return out.transpose(1, 2) if layout == "blhd" else out
+
+
+def _rope_table(cos: torch.Tensor, sin: torch.Tensor, rotary_dim: int, device=None) -> RopeTable:
+    """cos / sin: device float32 [n_pos, rotary_dim / 2], row-major."""
+    for t in (cos, sin):
+        if t.dtype != torch.float32 or not t.is_cuda or t.dim() != 2 or not t.is_contiguous():
+            raise SdpaError(-1, "rope tables must be contiguous float32 device tensors [n_pos, rotary_dim / 2]")
+        if t.shape[1] != rotary_dim // 2 or t.shape != cos.shape:
+            raise SdpaError(-1, f"rope tables {tuple(t.shape)} do not match rotary_dim {rotary_dim}")
+    return RopeTable(int(rotary_dim), cos.data_ptr(), sin.data_ptr(), int(cos.shape[0]))
+
+
+def rope(x: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor, rotary_dim: int, *, pos0: int = 0,
+         out: Optional[torch.Tensor] = None, layout: str = "bhld") -> torch.Tensor:
+    """Rotary embedding of x ([B, H, L, D], or [B, L, H, D] with layout="blhd")
+    through libsdpa.so: columns [0, rotary_dim) turn in (j, j + rotary_dim/2)
+    pairs by the table angles of position pos0 + l.  out=x rotates in place."""
+    lib = load()
+    if layout == "blhd":
+        x = x.transpose(1, 2)
+        if out is not None:
+            out = out.transpose(1, 2)
+    elif layout != "bhld":
+        raise ValueError(layout)
+    if out is None:
+        out = torch.empty_like(x)
+    if not x.is_cuda or x.dim() != 4 or tuple(out.shape) != tuple(x.shape) or out.dtype != x.dtype:
+        raise SdpaError(-1, "rope: x and out must be 4-D device tensors of one shape and dtype")
+    B, H, L, D = x.shape
+    table = _rope_table(cos, sin, rotary_dim)
+    st = lib.sdpa_rope(x.data_ptr(), _strides(x), out.data_ptr(), _strides(out), B, H, L, D, dtype_code(x.dtype),
+                       ctypes.byref(table), int(pos0), torch.cuda.current_stream(x.device).cuda_stream)
+    if st != 0:
+        raise SdpaError(st, f"sdpa_rope(B={B}, H={H}, L={L}, D={D}, R={rotary_dim}, pos0={pos0})")
     return out.transpose(1, 2) if layout == "blhd" else out

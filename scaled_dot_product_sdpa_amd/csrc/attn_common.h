@@ -62,6 +62,12 @@ struct Params {
     int col_groups;   // decode: column groups per kv head
     int kbase;        // decode: first key of split 0 (keys before it are masked for every row)
     int window;       // MASK_SLIDE: keys per query (>= 1)
+    // rotary embedding of Q (0 = none): columns [0, rope_dim) of query row i
+    // turn by the table angles of position rope_pos0 + i ([n_pos][rope_dim / 2] fp32)
+    int rope_dim;
+    int rope_pos0;
+    const float* rope_cos;
+    const float* rope_sin;
 };
 
 template <class To, class From>
@@ -93,6 +99,8 @@ struct TBF16 {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8_t>(a), bitcast<bf16x8_t>(b), c, 0, 0, 0);
     }
     static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16(a, b); }
+    static __device__ __forceinline__ float unpack_lo(uint32_t u) { return __uint_as_float(u << 16); }
+    static __device__ __forceinline__ float unpack_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
     static __device__ __forceinline__ void store4(void* dst, f32x4_t x) {
         u32x2_t w = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
         *reinterpret_cast<u32x2_t*>(dst) = w;
@@ -108,6 +116,10 @@ struct TF16 {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<f16x8_t>(a), bitcast<f16x8_t>(b), c, 0, 0, 0);
     }
     static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16(a, b); }
+    static __device__ __forceinline__ float unpack_lo(uint32_t u) { return (float)bitcast<_Float16>((uint16_t)u); }
+    static __device__ __forceinline__ float unpack_hi(uint32_t u) {
+        return (float)bitcast<_Float16>((uint16_t)(u >> 16));
+    }
     static __device__ __forceinline__ void store4(void* dst, f32x4_t x) {
         u32x2_t w = {pack_f16(x[0], x[1]), pack_f16(x[2], x[3])};
         *reinterpret_cast<u32x2_t*>(dst) = w;

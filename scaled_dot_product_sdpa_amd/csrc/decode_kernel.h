@@ -23,6 +23,7 @@
 #pragma once
 
 #include "attn_common.h"
+#include "rope_kernel.h"
 
 namespace sdpa_dev {
 
@@ -46,7 +47,7 @@ struct DecCfg {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <class TR, class C, int MASK>
+template <class TR, class C, int MASK, bool ROPE = false>
 __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
     constexpr int D = C::D, DO = C::DO, NW = C::NW, KS = C::KS;
     constexpr float NEG_INF = -__builtin_inff();
@@ -85,6 +86,11 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
         for (int i = 0; i < C::NCH; ++i) {
             const int d = 32 * i + 8 * g;
             qf[i] = (rv && d < D) ? *reinterpret_cast<const u32x4_t*>(qrow + d * 2) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        if constexpr (ROPE) {  // rotary embedding of the query row (columns < rope_dim)
+            if (rv)
+                rope_q_fragments<TR, C::NCH, 32>(qf, qrow, 8 * g, p.rope_dim, p.rope_cos, p.rope_sin,
+                                                 (int64_t)p.rope_pos0 + qi);
         }
     }
     // zero V^T pad rows [DO, DV) once (they feed the last O^T block)

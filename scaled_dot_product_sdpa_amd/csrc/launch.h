@@ -25,6 +25,8 @@ struct TileInfo {
 struct KernelSet {
     launch_fn full[sdpa_dev::MASK_VARIANTS];    // indexed by kernel mask variant (MASK_*)
     launch_fn decode[sdpa_dev::MASK_VARIANTS];  // indexed by kernel mask variant (MASK_*)
+    launch_fn full_rope[sdpa_dev::MASK_VARIANTS];    // the same with the rotary prologue on Q (16-bit only)
+    launch_fn decode_rope[sdpa_dev::MASK_VARIANTS];
     launch_fn combine;
     TileInfo full_cfg;
     TileInfo dec_cfg;

@@ -23,6 +23,7 @@
 #pragma once
 
 #include "attn_common.h"
+#include "rope_kernel.h"
 
 namespace sdpa_dev {
 
@@ -49,7 +50,7 @@ struct PfCfg {
 
 template <bool B> struct PfTag { static constexpr bool value = B; };
 
-template <class TR, class C, int MASK>
+template <class TR, class C, int MASK, bool ROPE = false>
 __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) {
     constexpr int D = C::D, BN = C::BN, BM = C::BM;
     constexpr float NEG_INF = -__builtin_inff();
@@ -128,6 +129,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         for (int ch = 0; ch < C::NCH; ++ch) {
             const int d = ch * 16 + hh * 8;
             qf[ch] = (rv && d < D) ? *reinterpret_cast<const u32x4_t*>(qrow + d * 2) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        if constexpr (ROPE) {  // rotary embedding of the query row (columns < rope_dim)
+            if (rv)
+                rope_q_fragments<TR, C::NCH, 16>(qf, qrow, hh * 8, p.rope_dim, p.rope_cos, p.rope_sin,
+                                                 (int64_t)p.rope_pos0 + qi);
         }
     }
 

@@ -24,6 +24,7 @@
 #pragma once
 
 #include "attn_common.h"
+#include "rope_kernel.h"
 
 namespace sdpa_dev {
 
@@ -69,7 +70,7 @@ struct R16Cfg {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <class TR, class C, int MASK>
+template <class TR, class C, int MASK, bool ROPE = false>
 __global__ __launch_bounds__(C::NT, 1) void prefill_r16_kernel(const Params p) {
     constexpr int D = C::D, BN = C::BN, NW = C::NW;
     constexpr float NEG_INF = -__builtin_inff();
@@ -155,6 +156,9 @@ __global__ __launch_bounds__(C::NT, 1) void prefill_r16_kernel(const Params p) {
 #pragma unroll
         for (int c = 0; c < C::NCH; ++c)
             qf[c] = *reinterpret_cast<const u32x4_t*>(qrow + (32 * c + 8 * g4) * 2);  // rows >= Lq read row 0, never stored
+        if constexpr (ROPE)  // rotary embedding of the query row (columns < rope_dim)
+            rope_q_fragments<TR, C::NCH, 32>(qf, qrow, 8 * g4, p.rope_dim, p.rope_cos, p.rope_sin,
+                                             (int64_t)p.rope_pos0 + (rv ? qi : 0));
     }
 
     const int rl = w * C::RPI + lane / C::KC;

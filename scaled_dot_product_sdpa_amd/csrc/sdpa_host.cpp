@@ -22,9 +22,11 @@
 
 #include "attn_kernel.h"
 #include "launch.h"
+#include "rope_kernel.h"
 
 using sdpa_dev::Params;
 using sdpa_host::KernelSet;
+using sdpa_host::launch_fn;
 
 namespace {
 
@@ -387,8 +389,8 @@ namespace {
 int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
                  sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len, int n_q_heads,
                  int n_kv_heads, int head_dim, int v_head_dim, sdpa_dtype dtype, float scale, sdpa_mask_kind mask_kind,
-                 const void* mask, sdpa_strides mask_st, sdpa_dtype mask_dtype, int window, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 const void* mask, sdpa_strides mask_st, sdpa_dtype mask_dtype, int window,
+                 const sdpa_rope_table* q_rope, int q_pos0, void* workspace, size_t workspace_bytes, void* stream) {
     sdpa_kernel kern;
     int reason;
     int st = select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype, mask_kind, &kern,
@@ -460,6 +462,18 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     p.scale_nonneg = scale >= 0.f;
     p.window = window;
     p.kbase = 0;
+    if (q_rope && q_rope->rotary_dim != 0) {
+        const int r = q_rope->rotary_dim;
+        if (dtype == SDPA_F32) return reject(SDPA_EUNSUPPORTED);  // the fp32 kernels take no rotary prologue
+        if (r < 0 || r % 64 != 0 || r > head_dim) return reject(SDPA_EUNSUPPORTED);
+        if (!q_rope->cos || !q_rope->sin || q_pos0 < 0 || (long)q_pos0 + q_len > (long)q_rope->n_pos)
+            return reject(SDPA_EINVAL);
+        if (((uintptr_t)q_rope->cos) % 16 != 0 || ((uintptr_t)q_rope->sin) % 16 != 0) return reject(SDPA_EUNSUPPORTED);
+        p.rope_dim = r;
+        p.rope_pos0 = q_pos0;
+        p.rope_cos = q_rope->cos;
+        p.rope_sin = q_rope->sin;
+    }
 
     const KernelSet* ks = kernel_set(dtype, head_dim, v_head_dim);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -495,8 +509,10 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         dim3 grid((unsigned)(8 * ((items + 7) / 8)), 1, 1);
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
                                     mask_kind, st, kern, reason));
+        const launch_fn f = p.rope_dim > 0 ? ks->full_rope[mk] : ks->full[mk];
+        if (!f) return reject(SDPA_EUNSUPPORTED);
         mark(0);
-        st = hip_status(ks->full[mk](p, grid, s));
+        st = hip_status(f(p, grid, s));
         if (st != SDPA_OK) return reject(st);
         mark(1);
         g_counters[1].fetch_add(1, std::memory_order_relaxed);
@@ -527,8 +543,10 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype, mask_kind,
                                 st, kern, reason));
     dim3 grid((unsigned)plan.splits, (unsigned)(n_kv_heads * plan.col_groups), (unsigned)batch);
+    const launch_fn f = p.rope_dim > 0 ? ks->decode_rope[mk] : ks->decode[mk];
+    if (!f) return reject(SDPA_EUNSUPPORTED);
     mark(0);
-    st = hip_status(ks->decode[mk](p, grid, s));
+    st = hip_status(f(p, grid, s));
     if (st != SDPA_OK) return reject(st);
     mark(1);
     dim3 cgrid((unsigned)rows, (unsigned)((v_head_dim + 63) / 64), 1);
@@ -549,8 +567,8 @@ int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     g_counters[0].fetch_add(1, std::memory_order_relaxed);
     if (mask_kind == SDPA_MASK_SLIDING) return reject(SDPA_EINVAL);  // needs a window: sdpa_forward_sliding
     return forward_impl(q, q_st, k, k_st, v, v_st, out, o_st, batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
-                        head_dim, dtype, scale, mask_kind, mask, mask_st, mask_dtype, 0, workspace, workspace_bytes,
-                        stream);
+                        head_dim, dtype, scale, mask_kind, mask, mask_st, mask_dtype, 0, nullptr, 0, workspace,
+                        workspace_bytes, stream);
 }
 
 int sdpa_forward_sliding(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
@@ -561,20 +579,63 @@ int sdpa_forward_sliding(const void* q, sdpa_strides q_st, const void* k, sdpa_s
     if (window < 1) return reject(SDPA_EINVAL);
     const sdpa_strides none{0, 0, 0, 0};
     return forward_impl(q, q_st, k, k_st, v, v_st, out, o_st, batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
-                        head_dim, dtype, scale, SDPA_MASK_SLIDING, nullptr, none, SDPA_F32, window, workspace,
-                        workspace_bytes, stream);
+                        head_dim, dtype, scale, SDPA_MASK_SLIDING, nullptr, none, SDPA_F32, window, nullptr, 0,
+                        workspace, workspace_bytes, stream);
 }
 
 int sdpa_forward_ex(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
                     sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len, int n_q_heads,
                     int n_kv_heads, int head_dim, int v_head_dim, sdpa_dtype dtype, float scale,
                     sdpa_mask_kind mask_kind, const void* mask, sdpa_strides mask_st, sdpa_dtype mask_dtype, int window,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    const sdpa_rope_table* q_rope, int q_pos0, void* workspace, size_t workspace_bytes, void* stream) {
     g_counters[0].fetch_add(1, std::memory_order_relaxed);
     if (mask_kind == SDPA_MASK_SLIDING && window < 1) return reject(SDPA_EINVAL);
     return forward_impl(q, q_st, k, k_st, v, v_st, out, o_st, batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
                         v_head_dim, dtype, scale, mask_kind, mask, mask_st, mask_dtype,
-                        mask_kind == SDPA_MASK_SLIDING ? window : 0, workspace, workspace_bytes, stream);
+                        mask_kind == SDPA_MASK_SLIDING ? window : 0, q_rope, q_pos0, workspace, workspace_bytes,
+                        stream);
+}
+
+int sdpa_rope(const void* x, sdpa_strides x_st, void* y, sdpa_strides y_st, int batch, int n_heads, int len,
+              int head_dim, sdpa_dtype dtype, const sdpa_rope_table* rope, int pos0, void* stream) {
+    if (batch <= 0 || n_heads <= 0 || len <= 0 || head_dim <= 0 || !rope || !x || !y) return SDPA_EINVAL;
+    if (dtype != SDPA_F32 && dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_EUNSUPPORTED;
+    const int r = rope->rotary_dim;
+    if (r <= 0 || r % 2 != 0 || r > head_dim) return SDPA_EINVAL;
+    if (!rope->cos || !rope->sin || pos0 < 0 || (long)pos0 + len > (long)rope->n_pos) return SDPA_EINVAL;
+    if (x_st.b < 0 || x_st.h < 0 || x_st.l < 0 || y_st.b < 0 || y_st.h < 0 || y_st.l < 0) return SDPA_EINVAL;
+    if (x_st.d != 1 || y_st.d != 1) return SDPA_EUNSUPPORTED;
+    const int es = elem_size(dtype);
+    const int64_t n[4] = {batch, n_heads, len, head_dim};
+    const bool same = x == y && x_st.b == y_st.b && x_st.h == y_st.h && x_st.l == y_st.l;
+    if (!same && overlaps(y, span_bytes(n, y_st, es), x, span_bytes(n, x_st, es))) return SDPA_EINVAL;
+    const int64_t total = (int64_t)batch * n_heads * len * head_dim;
+    if ((total + 255) / 256 > 0x7fffffffLL) return SDPA_EUNSUPPORTED;
+    sdpa_dev::RopeArgs a{};
+    a.x = x;
+    a.y = y;
+    const int64_t xs[4] = {x_st.b, x_st.h, x_st.l, x_st.d}, ys[4] = {y_st.b, y_st.h, y_st.l, y_st.d};
+    for (int i = 0; i < 4; ++i) {
+        a.xs[i] = xs[i];
+        a.ys[i] = ys[i];
+    }
+    a.B = batch;
+    a.H = n_heads;
+    a.L = len;
+    a.D = head_dim;
+    a.R = r;
+    a.pos0 = pos0;
+    a.cos = rope->cos;
+    a.sin = rope->sin;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (dtype == SDPA_F32)
+        hipLaunchKernelGGL(sdpa_dev::rope_kernel<float>, grid, dim3(256), 0, s, a);
+    else if (dtype == SDPA_F16)
+        hipLaunchKernelGGL(sdpa_dev::rope_kernel<_Float16>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(sdpa_dev::rope_kernel<__bf16>, grid, dim3(256), 0, s, a);
+    return hip_status(hipGetLastError());
 }
 
 }  // extern "C"

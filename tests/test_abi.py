@@ -148,3 +148,27 @@ def test_forward_rejects_bad_arguments_before_touching_the_gpu(lib):
     assert after["calls"] - before["calls"] == 16
     assert after["rejected"] - before["rejected"] == 16
     assert after["calls"] == after["full"] + after["vector"] + after["rejected"]
+
+
+def test_rope_arguments_are_checked_before_touching_the_gpu(lib):
+    S = _lib.Strides
+    st = S(2 * 16 * 64, 16 * 64, 64, 1)
+    tab = _lib.RopeTable(64, 4096, 8192, 32)
+
+    def ex(table, dt=2, pos0=0, d=64):
+        return lib.sdpa_forward_ex(4096, st, 4096, st, 4096, st, 1 << 20, st, 2, 16, 16, 16, 16, d, d, dt, 0.125,
+                                   3, None, S(0, 0, 0, 0), 0, 0, ctypes.byref(table), pos0, None, 0, None)
+    assert ex(_lib.RopeTable(32, 4096, 8192, 32)) == -2               # rotary_dim not a multiple of 64
+    assert ex(_lib.RopeTable(128, 4096, 8192, 32)) == -2              # rotary_dim > head_dim
+    assert ex(tab, dt=0) == -2                                        # fp32 kernels have no rotary prologue
+    assert ex(_lib.RopeTable(64, None, 8192, 32)) == -1               # missing table
+    assert ex(tab, pos0=17) == -1                                     # positions past the table
+    assert ex(tab, pos0=-1) == -1
+    assert ex(_lib.RopeTable(64, 4100, 8192, 32)) == -2               # table not 16-byte aligned
+    rope = lambda t, **kw: lib.sdpa_rope(4096, st, kw.get("y", 1 << 20), st, 2, 16, 16, 64, kw.get("dt", 2),
+                                         ctypes.byref(t), kw.get("pos0", 0), None)
+    assert rope(_lib.RopeTable(7, 4096, 8192, 32)) == -1              # odd rotary_dim
+    assert rope(_lib.RopeTable(66, 4096, 8192, 32)) == -1             # wider than the head
+    assert rope(tab, pos0=20) == -1                                   # positions past the table
+    assert rope(tab, y=4096 + 64) == -1                               # partial overlap of x and y
+    assert rope(tab, dt=3) == -2                                      # u8 is a mask type only
