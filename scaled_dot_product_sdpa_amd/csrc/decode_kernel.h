@@ -43,6 +43,7 @@ struct DecCfg {
     static constexpr int CPR = DO / 8;               // 16-byte chunks per V row
     static constexpr int VU = (4 * CPR + 63) / 64;   // (4-key, 8-column) V units per lane
     static constexpr int LDS = DV * TP * 2 + 16 * PP * 2 + 2 * NW * 16 * 4;
+    static constexpr bool PREFETCH = D <= 256;       // registers for a second chunk in flight
     static_assert(D % 8 == 0 && DO % 8 == 0, "head dims must be whole numbers of 16-byte chunks");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
@@ -77,48 +78,31 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
     const __amdgpu_buffer_rsrc_t vrs =
         make_rsrc(vglob, kend > 0 ? (uint32_t)(kend - 1) * vstep32 + (uint32_t)(DO * 2) : 0u);
 
-    // Q fragments (B operand): row col, head-dim columns 32 i + 8 g .. +7
-    u32x4_t qf[C::NCH];
-    {
-        const char* qrow = reinterpret_cast<const char*>(p.q) +
-                           ((int64_t)b * p.qs[0] + (int64_t)qh * p.qs[1] + (int64_t)qi * p.qs[2]) * 2;
-#pragma unroll
-        for (int i = 0; i < C::NCH; ++i) {
-            const int d = 32 * i + 8 * g;
-            qf[i] = (rv && d < D) ? *reinterpret_cast<const u32x4_t*>(qrow + d * 2) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-        if constexpr (ROPE) {  // rotary embedding of the query row (columns < rope_dim)
-            if (rv)
-                rope_q_fragments<TR, C::NCH, 32>(qf, qrow, 8 * g, p.rope_dim, p.rope_cos, p.rope_sin,
-                                                 (int64_t)p.rope_pos0 + qi);
-        }
-    }
-    // zero V^T pad rows [DO, DV) once (they feed the last O^T block)
-    if constexpr (C::DV > DO) {
-        for (int idx = tid; idx < (C::DV - DO) * C::TP; idx += C::NT) Vt[DO * C::TP + idx] = 0;
-    }
     const int64_t mrow = HAS_MT ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)qi * p.ms[2] : 0;
-    const float c_scale = p.scale_log2;
 
-    float m_run = NEG_INF, l_run = 0.f;
-    f32x4_t oacc[C::NDBW];
-#pragma unroll
-    for (int i = 0; i < C::NDBW; ++i) oacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int k0 = kbeg; k0 < kend; k0 += KS) {
-        const int kw = k0 + 16 * w;  // this wave's first key
-        // ---- 1. issue every load of the chunk ----
-        u32x4_t kf[C::NCH];
+    // ---- loads of one chunk (keys k0 .. k0 + KS - 1): this wave's 16 keys of
+    // K as A operands (lane: key col, head-dim columns 32 i + 8 g .. +7), its
+    // V rows bound for LDS and, for mask tensors, its mask groups ----
+    u32x4_t kf[C::NCH];
+    // V unit u of this lane: keys kw + 4 * q4 .. +3, head-dim columns 8 c .. +7
+    // (the key quad varies fastest across lanes, so the transposed LDS stores
+    // of one instruction spread over 16 column groups x 4 quads of banks)
+    u32x4_t vr[C::VU][4];
+    typename MaskRaw<MASK>::type mr{};
+    // (K first: loads return in order, and S = K Q^T waits only for K, Q and
+    // the mask while V is still arriving)
+    auto issue_k = [&](int k0) __attribute__((always_inline)) {
+        const int kw = k0 + 16 * w;
 #pragma unroll
         for (int i = 0; i < C::NCH; ++i) {
             const int d = 32 * i + 8 * g;
             kf[i] = u32x4_t{0u, 0u, 0u, 0u};
             if (d < D) kf[i] = buffer_load16(krs, (uint32_t)(kw + col) * kstep32 + (uint32_t)(d * 2));
         }
-        // V unit u of this lane: keys kw + 4 * q4 .. +3, head-dim columns 8 c .. +7
-        // (the key quad varies fastest across lanes, so the transposed LDS stores
-        // of one instruction spread over 16 column groups x 4 quads of banks)
-        u32x4_t vr[C::VU][4];
+    };
+    auto issue_v = [&](int k0) __attribute__((always_inline)) {
+        const int kw = k0 + 16 * w;
+        if constexpr (HAS_MT) mr = load_mask_group<MASK>(p, mrow, kw + 4 * g);
 #pragma unroll
         for (int u = 0; u < C::VU; ++u) {
             const int idx = lane + 64 * u;
@@ -130,8 +114,49 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
                     vr[u][e] = buffer_load16(vrs, (uint32_t)(kw + 4 * q4 + e) * vstep32 + (uint32_t)(c * 16));
             }
         }
-        typename MaskRaw<MASK>::type mr{};
-        if constexpr (HAS_MT) mr = load_mask_group<MASK>(p, mrow, kw + 4 * g);
+    };
+    // with prefetching, the first chunk's K loads go out before anything else
+    // (its V loads right after Q's)
+    if constexpr (C::PREFETCH) {
+        if (kbeg < kend) issue_k(kbeg);
+    }
+
+    // Q fragments (B operand): row col, head-dim columns 32 i + 8 g .. +7;
+    // rows past n_rep * Lq read row 0 (their results are never stored)
+    u32x4_t qf[C::NCH];
+    {
+        const char* qrow = reinterpret_cast<const char*>(p.q) +
+                           ((int64_t)b * p.qs[0] + (int64_t)qh * p.qs[1] + (int64_t)qi * p.qs[2]) * 2;
+#pragma unroll
+        for (int i = 0; i < C::NCH; ++i) {
+            const int d = 32 * i + 8 * g;
+            const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qrow + min(d, D - 8) * 2);
+            qf[i] = d < D ? x : u32x4_t{0u, 0u, 0u, 0u};
+        }
+        if constexpr (ROPE)  // rotary embedding of the query row (columns < rope_dim)
+            rope_q_fragments<TR, C::NCH, 32>(qf, qrow, 8 * g, p.rope_dim, p.rope_cos, p.rope_sin,
+                                             (int64_t)p.rope_pos0 + qi);
+    }
+    if constexpr (C::PREFETCH) {
+        if (kbeg < kend) issue_v(kbeg);
+    }
+    // zero V^T pad rows [DO, DV) once (they feed the last O^T block)
+    if constexpr (C::DV > DO) {
+        for (int idx = tid; idx < (C::DV - DO) * C::TP; idx += C::NT) Vt[DO * C::TP + idx] = 0;
+    }
+    const float c_scale = p.scale_log2;
+
+    float m_run = NEG_INF, l_run = 0.f;
+    f32x4_t oacc[C::NDBW];
+#pragma unroll
+    for (int i = 0; i < C::NDBW; ++i) oacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = kbeg; k0 < kend; k0 += KS) {
+        const int kw = k0 + 16 * w;  // this wave's first key
+        if constexpr (!C::PREFETCH) {
+            issue_k(k0);
+            issue_v(k0);
+        }
 
         // ---- 2. S^T = K Q^T (lane: row col, keys kw + 4 g + e) ----
         f32x4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -174,6 +199,14 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
                             u32x2_t{lo, hi};
                     }
                 }
+            }
+        }
+        // K, V and the mask of this chunk are consumed: the next chunk's loads
+        // overlap this chunk's softmax and P V
+        if constexpr (C::PREFETCH) {
+            if (k0 + KS < kend) {
+                issue_k(k0 + KS);
+                issue_v(k0 + KS);
             }
         }
         __syncthreads();
