@@ -51,6 +51,7 @@ struct Params {
     int64_t ms[4];
     int mask_dtype;   // MDT_*
     int mask_vec;     // 1: key stride 1 and 4-element runs aligned -> vector loads
+    int64_t mask_span;  // bytes from `mask` to one past its last element
     int B, Lq, Lk, Hq, Hkv, n_rep;
     float scale_log2;  // scale * log2(e)
     int scale_nonneg;  // scale >= 0: the row max can be taken on unscaled scores
@@ -230,6 +231,37 @@ __device__ __forceinline__ typename MaskRaw<MASK>::type load_mask_group(const Pa
         }
     }
     return r;
+}
+
+// The same group through a buffer resource whose range ends at the mask's
+// last byte (mask_vec layouts only): one vector load, no branch; bytes past
+// the range read as zero.
+template <int MASK>
+__device__ __forceinline__ typename MaskRaw<MASK>::type load_mask_group_rs(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (MASK == MASK_BOOL) return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    else if constexpr (MASK == MASK_ADD16) return bitcast<u32x2_t>(__builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    else return bitcast<u32x4_t>(__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Any other layout: the group's 4 elements one by one (element offsets
+// row_off + (key0 + k) * key_stride), through the same kind of resource.
+template <int MASK>
+__device__ __forceinline__ typename MaskRaw<MASK>::type load_mask_group_rs_strided(__amdgpu_buffer_rsrc_t r,
+                                                                                    uint32_t row_off, int key0,
+                                                                                    uint32_t key_stride) {
+    typename MaskRaw<MASK>::type g{};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t e = row_off + (uint32_t)(key0 + k) * key_stride;
+        if constexpr (MASK == MASK_BOOL) {
+            g |= (__builtin_amdgcn_raw_buffer_load_b8(r, e, 0, 0) ? 1u : 0u) << (8 * k);
+        } else if constexpr (MASK == MASK_ADD16) {
+            g[k >> 1] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, e * 2, 0, 0) << (16 * (k & 1));
+        } else {
+            g[k] = __builtin_amdgcn_raw_buffer_load_b32(r, e * 4, 0, 0);
+        }
+    }
+    return g;
 }
 
 // Additive mask value of key k (0..3) of a raw group, widened to float.

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     constexpr bool HAS_MT = (MASK == MASK_ADD16 || MASK == MASK_ADD32 || MASK == MASK_BOOL);
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wm = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wm = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, hh = lane >> 5;
 
     // ---- work item (XCD-aware, longest causal tiles first) ----
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         const int lo = min(qmin + 31, p.Lq - 1) + off - p.window + 1;  // window's left edge, wave's last row
         tp0 = max(t0, lo <= 0 ? 0 : (lo + BN - 1) / BN);
     }
-    if (HAS_MT || !p.scale_nonneg) tp1 = tp0;
+    if (HAS_MT) tp1 = tp0;
     tp0 = min(tp0, ntiles);
     tp1 = max(tp0, min(tp1, ntiles));
 
@@ -134,6 +134,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
             if (rv)
                 rope_q_fragments<TR, C::NCH, 16>(qf, qrow, hh * 8, p.rope_dim, p.rope_cos, p.rope_sin,
                                                  (int64_t)p.rope_pos0 + qi);
+        }
+        // a negative scale runs as |scale| on -Q (exact: a sign flip) and a zero
+        // scale as scale 1 on Q = 0 (every score is 0 either way), so the scale
+        // is positive and the row max can always be taken on unscaled scores
+        if (p.scale_log2 < 0.f) {
+#pragma unroll
+            for (int ch = 0; ch < C::NCH; ++ch) qf[ch] ^= 0x80008000u;
+        } else if (p.scale_log2 == 0.f) {
+#pragma unroll
+            for (int ch = 0; ch < C::NCH; ++ch) qf[ch] = u32x4_t{0u, 0u, 0u, 0u};
         }
     }
 
@@ -172,14 +182,36 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         }
     };
 
-    const int64_t mrow = HAS_MT ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)(rv ? qi : 0) * p.ms[2] : 0;
+    // mask rows: rows past Lq read row Lq - 1 (never stored).  One buffer
+    // resource per wave starts at the wave's first row and ends at the mask's
+    // last byte (32-bit element offsets within it: checked on the host), so
+    // every group is one branch-free vector load (or four scalar ones).
+    constexpr int MES = MASK == MASK_BOOL ? 1 : (MASK == MASK_ADD16 ? 2 : 4);
+    const int q0c = min(qmin, p.Lq - 1), qic = min(qi, p.Lq - 1);
+    const int64_t mbase = HAS_MT ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)q0c * p.ms[2] : 0;
+    const uint32_t mlane = HAS_MT ? (uint32_t)((qic - q0c) * p.ms[2]) : 0u;
+    const int64_t mleft = HAS_MT ? p.mask_span - mbase * MES : 0;
+    const __amdgpu_buffer_rsrc_t mrs =
+        make_rsrc(HAS_MT ? reinterpret_cast<const char*>(p.mask) + mbase * MES : nullptr,
+                  (uint32_t)(mleft > 0xffffffffLL ? 0xffffffffLL : mleft));
     typename MaskRaw<MASK>::type mr[HAS_MT ? C::NKB : 1][4];
     auto load_mask = [&](int kt) {
         if constexpr (HAS_MT) {
+            if (p.mask_vec) {
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb)
+                for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) mr[kb][a4] = load_mask_group<MASK>(p, mrow, kt + kb * 32 + 8 * a4 + 4 * hh);
+                    for (int a4 = 0; a4 < 4; ++a4)
+                        mr[kb][a4] = load_mask_group_rs<MASK>(
+                            mrs, (mlane + (uint32_t)(kt + kb * 32 + 8 * a4 + 4 * hh)) * MES);
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+                    for (int a4 = 0; a4 < 4; ++a4)
+                        mr[kb][a4] = load_mask_group_rs_strided<MASK>(mrs, mlane, kt + kb * 32 + 8 * a4 + 4 * hh,
+                                                                      (uint32_t)p.ms[3]);
+            }
         }
     };
 
@@ -187,7 +219,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     f32x16_t oacc[C::NDB];
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16_t{};
-    const float c_scale = p.scale_log2;
+    const float c_scale = p.scale_log2 == 0.f ? 1.f : __builtin_fabsf(p.scale_log2);
 
     // S^T of one tile from LDS stage `stage`
     auto scores = [&](int stage, f32x16_t (&sacc)[C::NKB]) {
@@ -253,9 +285,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     };
 
     // one key tile; the mask-free and the masked variants run as separate loops
-    // so neither carries the other's code (or register copies) around its body
-    auto tile = [&](int it, auto masked_tag) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
+    // so neither carries the other's code (or register copies) around its body.
+    // TAIL: the last tile of a mask-free or mask-tensor workgroup, whose keys
+    // may run past the end (causal and sliding masks exclude them already).
+    auto tile = [&](int it, auto masked_tag, auto tail_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_tag)::value, TAIL = decltype(tail_tag)::value;
         const int kt = it * BN, stage = it & 1;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();  // tile `it` is in LDS; every wave is done with the other stage
@@ -271,42 +305,60 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
             softmax_pv(stage, sacc, mx * c_scale, c_scale);
         } else {
-            float mtile = NEG_INF;
+            constexpr bool ADD = (MASK == MASK_ADD16 || MASK == MASK_ADD32);
+            // per-element mask; RAW: on unscaled scores (the scale is positive,
+            // so a masked -inf stays -inf once scaled); additive masks add to
+            // scaled scores
+            auto mask_scores = [&](auto raw_tag) __attribute__((always_inline)) {
+                constexpr bool RAW = decltype(raw_tag)::value;
+                float mtile = NEG_INF;
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) {
+                for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
+                    for (int a4 = 0; a4 < 4; ++a4) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = kt + kb * 32 + 8 * a4 + 4 * hh + r;
-                        float x = sacc[kb][4 * a4 + r] * c_scale;
-                        bool ok = j < kend;
-                        if constexpr (MASK == MASK_ADD16 || MASK == MASK_ADD32)
-                            x = __builtin_fmaf(mask_value<MASK>(mr[kb][a4], r, p.mask_dtype), kLog2e, x);
-                        if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
-                        if constexpr (MASK == MASK_SLIDE) ok = ok && in_window(j, qi + off, p.window);
-                        if constexpr (MASK == MASK_BOOL) ok = ok && ((mr[kb][a4] >> (8 * r)) & 0xffu) != 0u;
-                        x = ok ? x : NEG_INF;
-                        sacc[kb][4 * a4 + r] = x;
-                        mtile = fmaxf(mtile, x);
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = kt + kb * 32 + 8 * a4 + 4 * hh + r;
+                            float x = sacc[kb][4 * a4 + r];
+                            if constexpr (!RAW) x *= c_scale;
+                            bool ok = true;
+                            if constexpr (TAIL) ok = j < kend;
+                            if constexpr (ADD)
+                                x = __builtin_fmaf(mask_value<MASK>(mr[kb][a4], r, p.mask_dtype), kLog2e, x);
+                            if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
+                            if constexpr (MASK == MASK_SLIDE) ok = ok && in_window(j, qi + off, p.window);
+                            if constexpr (MASK == MASK_BOOL) ok = ok && ((mr[kb][a4] >> (8 * r)) & 0xffu) != 0u;
+                            x = ok ? x : NEG_INF;
+                            sacc[kb][4 * a4 + r] = x;
+                            mtile = fmaxf(mtile, x);
+                        }
                     }
                 }
-            }
+                return mtile;
+            };
+            const float mt = mask_scores(PfTag<!ADD>{});
             if (it + 1 < ntiles) load_mask(kt + BN);
-            softmax_pv(stage, sacc, mtile, 1.f);
+            if constexpr (ADD) softmax_pv(stage, sacc, mt, 1.f);
+            else softmax_pv(stage, sacc, mt * c_scale, c_scale);
         }
     };
 
     // masked tiles left of the plain range (window edge), plain tiles, masked
     // tiles right of it (diagonal, ragged end, or every tile of a mask tensor)
+    constexpr bool TAIL_CHECK = !CAUSAL_END;
     int it = t0;
     if (it < ntiles) issue_tile(it * BN, it & 1);
     if constexpr (!HAS_MT) {
-        for (; it < tp0; ++it) tile(it, PfTag<true>{});
-        for (; it < tp1; ++it) tile(it, PfTag<false>{});
+        for (; it < tp0; ++it) tile(it, PfTag<true>{}, PfTag<false>{});
+        for (; it < tp1; ++it) tile(it, PfTag<false>{}, PfTag<false>{});
     }
     if (it < ntiles) load_mask(it * BN);
-    for (; it < ntiles; ++it) tile(it, PfTag<true>{});
+    if constexpr (TAIL_CHECK) {
+        for (; it < ntiles - 1; ++it) tile(it, PfTag<true>{}, PfTag<false>{});
+        if (it < ntiles) tile(it, PfTag<true>{}, PfTag<true>{});
+    } else {
+        for (; it < ntiles; ++it) tile(it, PfTag<true>{}, PfTag<false>{});
+    }
 
     // ---- epilogue ----
     float lsum_row;

@@ -429,10 +429,16 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         if (mask_st.b < 0 || mask_st.h < 0 || mask_st.l < 0 || mask_st.d < 0) return reject(SDPA_EINVAL);
         const int mes = elem_size(mask_dtype);
         if (((uintptr_t)mask) % mes != 0) return reject(SDPA_EUNSUPPORTED);
+        // Mask offsets within a wave's rows are 32-bit: 64 rows plus one tile
+        // past the last key must stay below 4 GiB.
+        if (((double)mask_st.l * 64.0 + (double)(kv_len + 256) * (double)mask_st.d) * mes >= 4294967295.0)
+            return reject(SDPA_EUNSUPPORTED);
         // Vector mask loads need 4-key runs aligned to 4 elements.
         mvec = mask_st.d == 1 && ((uintptr_t)mask) % (4 * mes) == 0 && mask_st.b % 4 == 0 && mask_st.h % 4 == 0 &&
                mask_st.l % 4 == 0;
         p.mask = mask;
+        const int64_t mn[4] = {batch, n_q_heads, q_len, kv_len};
+        p.mask_span = (int64_t)span_bytes(mn, mask_st, mes);
         p.ms[0] = mask_st.b;
         p.ms[1] = mask_st.h;
         p.ms[2] = mask_st.l;

@@ -184,3 +184,44 @@ def test_decode_qk192_v128(gpu_lib, dtype, mask_kind, lq, lk):
     out = run_gpu(c)
     assert tuple(out.shape) == (1, 16, lq, 128)
     assert_parity(out, oracle_out(c), dtype, f"decode qk192/v128 {dtype} {mask_kind} Lq={lq} Lk={lk}")
+
+
+# --------------------------------------------------------------------------
+# Zero and negative scales (the 16-bit prefill kernel runs them as a positive
+# scale on Q = 0 / -Q): every kernel family, masks with and without tensors.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("scale", [0.0, -0.3])
+@pytest.mark.parametrize("mask_kind", ["none", "causal", "boolean", "additive"])
+@pytest.mark.parametrize("D,lq,dtype", [(72, 150, "bf16"), (128, 100, "f16"), (256, 90, "bf16"), (512, 70, "bf16"),
+                                        (64, 3, "bf16"), (64, 100, "f32")])
+def test_zero_and_negative_scale(gpu_lib, D, lq, dtype, mask_kind, scale):
+    c = si.make_case(1, 4, 2, lq, 130, D, dtype=dtype, layout="bhld", mask_kind=mask_kind, seed=D + lq,
+                     scale=scale, mask_shape="qk", mask_p=0.3)
+    assert_parity(run_gpu(c), oracle_out(c), dtype, f"scale={scale} D={D} Lq={lq} {dtype} {mask_kind}")
+
+
+# --------------------------------------------------------------------------
+# Mask tensors in layouts without the vector fast path: keys strided (a
+# transposed view), rows not a multiple of 4 elements apart, misaligned base.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", ["key_strided", "odd_rows", "offset_base"])
+@pytest.mark.parametrize("mask_kind", ["boolean", "additive"])
+@pytest.mark.parametrize("D,lq", [(72, 150), (128, 70), (256, 90), (64, 5)])
+def test_mask_layouts_without_vector_loads(gpu_lib, D, lq, mask_kind, layout):
+    lk = 131 if layout == "odd_rows" else 132
+    c = si.make_case(1, 4, 2, lq, lk, D, dtype="bf16", layout="bhld", mask_kind=mask_kind, seed=D + lq,
+                     mask_shape="qk", mask_p=0.3)
+    q, k, v, _ = to_device(c)
+    m = c.mask
+    if layout == "key_strided":
+        dm = m.transpose(-1, -2).contiguous().cuda().transpose(-1, -2)
+    elif layout == "offset_base":
+        flat = torch.zeros(m.numel() + 1, dtype=m.dtype)
+        flat[1:] = m.reshape(-1)
+        dm = flat.cuda()[1:].view(m.shape)
+    else:
+        dm = m.cuda()
+    assert torch.equal(dm.cpu(), m)
+    out = gpu_lib.forward(q, k, v, scale=c.scale, mask=dm, mask_kind=mask_kind)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_out(c), "bf16", f"mask layout {layout} {mask_kind} D={D} Lq={lq}")
