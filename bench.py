@@ -58,8 +58,8 @@ PRIMARY = "decode-d256-lk4096"
 KERNEL_SOURCES = {
     "decode": ["attn_common.h", "decode_kernel.h", "attn_kernel.h", "launch.h", "inst_template.hip.in"],
     "prefill72": ["attn_common.h", "prefill_kernel.h", "launch.h", "inst_template.hip.in"],
-    "prefill512": ["attn_common.h", "prefill_wide_kernel.h", "launch.h", "inst_template.hip.in"],
-    "sliding": ["attn_common.h", "prefill_wide_kernel.h", "decode_kernel.h", "attn_kernel.h", "launch.h",
+    "prefill512": ["attn_common.h", "prefill_sd_kernel.h", "launch.h", "inst_template.hip.in"],
+    "sliding": ["attn_common.h", "prefill_sd_kernel.h", "decode_kernel.h", "attn_kernel.h", "launch.h",
                 "inst_template.hip.in"],
     "decode_dv": ["attn_common.h", "decode_kernel.h", "attn_kernel.h", "launch.h", "inst_pair_template.hip.in"],
     "tiny": ["attn_common.h", "attn_kernel.h", "tile_configs.h", "launch.h", "inst_template.hip.in"],

@@ -22,7 +22,8 @@
 //     and the transposed 64-bit V reads (4 rows x 4 chunks) on distinct banks.
 // Per tile and wave, LDS reads are 2 * BN * (D / NS) * 2 bytes for a
 // 32 x BN x D / NS share of the work: at D = 512, NS = 2, 40 KB per MFLOP
-// including the score exchange, against 64 KB for 16-row waves.
+// including the score exchange, against 64 KB for 16-row waves.  At D = 256
+// one wave holds all 256 columns (NS = 1, no exchange): 32 KB per MFLOP.
 #pragma once
 
 #include "attn_common.h"
@@ -52,6 +53,7 @@ struct SdCfg {
     static constexpr int NI = BN * KC / (64 * NW);  // loads per wave per tile (K; V the same)
     static constexpr int XB = NS > 1 ? NW * NKB * 64 * 16 * 4 : 0;  // partial-score exchange
     static constexpr int LDS = 4 * TILEB + XB;
+    static constexpr int WPE = 2;          // waves per SIMD the registers must allow
     static_assert(NS == 1 || NS == 2, "head-dim split");
     static_assert(DH % 128 == 0 && KC <= 64 && 64 % KC == 0, "head dim");
     static_assert(BN % 32 == 0 && (BN * KC) % (64 * NW) == 0, "key tile");
@@ -60,7 +62,7 @@ struct SdCfg {
 };
 
 template <class TR, class C, int MASK, bool ROPE = false>
-__global__ __launch_bounds__(C::NT, 1) void prefill_sd_kernel(const Params p) {
+__global__ __launch_bounds__(C::NT, C::WPE) void prefill_sd_kernel(const Params p) {
     constexpr int D = C::D, BN = C::BN, NW = C::NW, NS = C::NS, DH = C::DH;
     constexpr float NEG_INF = -__builtin_inff();
     constexpr float kRescale = 8.0f;
