@@ -190,7 +190,28 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* addr) {
 #endif
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Cross-lane exchanges without an LDS round trip.  v_permlane32_swap on (x, x)
+// leaves lane i holding (x[i mod 32], x[i mod 32 + 32]) and v_permlane16_swap
+// (x[i & ~16], x[i | 16]) for each 32-lane half: both partners of an xor-32
+// (xor-16) pair, in the same order in both lanes of the pair.
+__device__ __forceinline__ f32x2_t pair32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return f32x2_t{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32x2_t pair16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return f32x2_t{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// the value of lane i ^ 32
+__device__ __forceinline__ float xor32(float x) {
+    const f32x2_t r = pair32(x);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+}
+// max / sum over lanes i and i ^ 32 (i ^ 16): the same float in both lanes
+__device__ __forceinline__ float max_x32(float x) { const f32x2_t r = pair32(x); return fmaxf(r[0], r[1]); }
+__device__ __forceinline__ float sum_x32(float x) { const f32x2_t r = pair32(x); return r[0] + r[1]; }
+__device__ __forceinline__ float max_x16(float x) { const f32x2_t r = pair16(x); return fmaxf(r[0], r[1]); }
+__device__ __forceinline__ float sum_x16(float x) { const f32x2_t r = pair16(x); return r[0] + r[1]; }
 
 // ---------------------------------------------------------------------------
 // Masks are read in groups of 4 consecutive keys (the 4 keys one lane holds

@@ -179,8 +179,7 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
             x[e] = ok ? t : NEG_INF;
             mx = fmaxf(mx, x[e]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = max_x32(max_x16(mx));
         if (g == 0) red[0][w][col] = mx;
         // V -> LDS transposed: 4 keys x 8 columns -> 8 rows of V^T, 4 keys (8 bytes) each
 #pragma unroll
@@ -224,8 +223,7 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
             pe[e] = fast_exp2(x[e] - muse);
             ls += pe[e];
         }
-        ls += __shfl_xor(ls, 16, 64);
-        ls += __shfl_xor(ls, 32, 64);
+        ls = sum_x32(sum_x16(ls));
         if (g == 0) red[1][w][col] = ls;
         *reinterpret_cast<u32x2_t*>(&Ps[col * C::PP + 16 * w + 4 * g]) =
             u32x2_t{TR::pack(pe[0], pe[1]), TR::pack(pe[2], pe[3])};

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     };
     // online softmax on scores already scaled (c_eff = 1) or raw (c_eff = scale)
     auto softmax_pv = [&](int stage, f32x16_t (&sacc)[C::NKB], float mtile, float c_eff) {
-        mtile = fmaxf(mtile, xor32(mtile));
+        mtile = max_x32(mtile);
         if (__any(mtile > m_run + kRescale)) {
             const float m_new = fmaxf(m_run, mtile);
             const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         const float y = xor32(x);
         lsum_row = (hh == HL) ? x : y;
     } else {
-        lsum_row = l_run + xor32(l_run);
+        lsum_row = sum_x32(l_run);
     }
     if (rv) {
         const float inv = lsum_row > 0.f ? 1.f / lsum_row : 0.f;

@@ -315,7 +315,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void prefill_sd_kernel(const Params 
         }
 
         // ---- online softmax (lazy rescale) ----
-        mtile = fmaxf(mtile, xor32(mtile));
+        mtile = max_x32(mtile);
         if (__any(mtile > m_run + kRescale)) {
             const float m_new = fmaxf(m_run, mtile);
             const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void prefill_sd_kernel(const Params 
     }
 
     // ---- epilogue: lane holds query col, columns DH hf + 32 db + 8 a4 + 4 hh .. +3 ----
-    const float lsum_row = l_run + xor32(l_run);
+    const float lsum_row = sum_x32(l_run);
     if (rv) {
         const float inv = lsum_row > 0.f ? 1.f / lsum_row : 0.f;
         char* orow = reinterpret_cast<char*>(p.o) +
