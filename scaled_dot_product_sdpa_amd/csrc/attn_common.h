@@ -177,6 +177,13 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
 #endif
 }
+// The same with a wave-uniform part of the offset in soffset (an SGPR).
+__device__ __forceinline__ void buffer_load16_lds_so(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff,
+                                                     uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
+#endif
+}
 
 // ds_read_b64_tr_b16: in each 16-lane group, output lane i element e is
 // element i % 4 of the 4 values at the address of source lane 4 e + i / 4.

@@ -172,11 +172,21 @@ __global__ __launch_bounds__(C::NT, C::WPE) void prefill_sd_kernel(const Params 
         char* vl = smem + (2 * stage + 1) * C::TILEB;
 #pragma unroll
         for (int u = 0; u < C::NI; ++u) {
+            // row = r0 + lane / KC: r0 (and, with one row per load, the swizzle) is
+            // wave-uniform and goes in soffset; only the chunk offset is per lane
             const int ins = u * NW + w;
-            const int row = ins * C::RPI + lane / C::KC;
-            const uint32_t cb = (uint32_t)(((lane % C::KC) ^ sd_sw(row)) * 16);
-            buffer_load16_lds(krs, kl + ins * 1024, (uint32_t)(kt + row) * kstep + cb);
-            buffer_load16_lds(vrs, vl + ins * 1024, (uint32_t)(kt + row) * vstep + cb);
+            const int r0 = ins * C::RPI;
+            uint32_t vk, vv;
+            if constexpr (C::RPI == 1) {
+                vk = vv = (uint32_t)(lane * 16) ^ (uint32_t)(sd_sw(r0) * 16);
+            } else {
+                const int row = r0 + lane / C::KC;
+                const uint32_t cb = (uint32_t)(((lane % C::KC) ^ sd_sw(row)) * 16);
+                vk = (uint32_t)(lane / C::KC) * kstep + cb;
+                vv = (uint32_t)(lane / C::KC) * vstep + cb;
+            }
+            buffer_load16_lds_so(krs, kl + ins * 1024, vk, (uint32_t)(kt + r0) * kstep);
+            buffer_load16_lds_so(vrs, vl + ins * 1024, vv, (uint32_t)(kt + r0) * vstep);
         }
     };
 
@@ -242,15 +252,24 @@ __global__ __launch_bounds__(C::NT, C::WPE) void prefill_sd_kernel(const Params 
         const char* vl = smem + (2 * stage + 1) * C::TILEB + vbase;
 
         // ---- S^T = K Q^T over this wave's head-dim share ----
+        // K reads run one step ahead of the MFMAs that use them (two operand
+        // buffers; the scheduling barrier keeps each read ahead of its MFMA)
         f32x16_t sacc[C::NKB];
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) {
+            auto kread = [&](int c) __attribute__((always_inline)) {
+                return *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * C::ROWB + (c >> 3) * 256 +
+                                                         ((32 * (c & 7)) ^ kxe));
+            };
+            u32x4_t ka[2];
+            ka[0] = kread(0);
             f32x16_t s = f32x16_t{};
 #pragma unroll
             for (int c = 0; c < C::NCH; ++c) {
-                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kl + kb * 32 * C::ROWB + (c >> 3) * 256 +
-                                                                    ((32 * (c & 7)) ^ kxe));
-                s = TR::mma(a, qf[c], s);
+                if (c + 1 < C::NCH) ka[(c + 1) & 1] = kread(c + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                s = TR::mma(ka[c & 1], qf[c], s);
+                __builtin_amdgcn_sched_barrier(0);
             }
             sacc[kb] = s;
         }
@@ -348,12 +367,21 @@ __global__ __launch_bounds__(C::NT, C::WPE) void prefill_sd_kernel(const Params 
 #pragma unroll
                 for (int q = 0; q < 4; ++q) bf[q] = TR::pack(sacc[kb][8 * pc + 2 * q], sacc[kb][8 * pc + 2 * q + 1]);
                 const char* vr = vl + (kb * 32 + 16 * pc) * C::ROWB;
-#pragma unroll
-                for (int db = 0; db < C::NDB; ++db) {
+                // V^T reads one block ahead of the MFMAs (two operand buffers)
+                auto vread = [&](int db) __attribute__((always_inline)) {
                     const char* va = vr + (db >> 2) * 256 + ((64 * (db & 3)) ^ vxe);
                     const u32x2_t y0 = lds_read_tr16(va);
                     const u32x2_t y1 = lds_read_tr16(va + vsec);
-                    oacc[db] = TR::mma(u32x4_t{y0[0], y0[1], y1[0], y1[1]}, bf, oacc[db]);
+                    return u32x4_t{y0[0], y0[1], y1[0], y1[1]};
+                };
+                u32x4_t vb[2];
+                vb[0] = vread(0);
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db) {
+                    if (db + 1 < C::NDB) vb[(db + 1) & 1] = vread(db + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    oacc[db] = TR::mma(vb[db & 1], bf, oacc[db]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
