@@ -456,98 +456,87 @@ __global__ __launch_bounds__(C::NT, C::OCC) void attn_tile_kernel(const Params p
     }
 }
 
-// Decode combine: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
-// One workgroup (4 waves) per (output row, 64-wide slice of d): lane l of
-// wave w reads float4 column group l % 16 of splits s = 4 * (16 * i + w) +
-// l / 16 ... so every partial load of the workgroup is in flight at once;
-// the four split phases of a wave and the four waves are then summed in a
-// fixed order (deterministic).  grid = (B*Hq*Lq, ceil(D/64)).
+// Decode combine: O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s, by one
+// wave per (output row, 64-wide slice of d), with no cross-wave step: lane l
+// takes float4 column group l % 16 and split phase l / 16 (splits
+// s = 4 i + l / 16 of each pass of 64), so the first pass's partial loads are
+// all in flight at once.  The (m, l) pairs go through LDS once (max, then the
+// weights, stored phase-major so each lane reads its 16 weights as four
+// 16-byte reads); the four phases are summed by lane swaps in a fixed order
+// (deterministic).  grid = (B*Hq*Lq, ceil(D/64)), 64 threads.
 constexpr int kMaxSplits = 1024;
 
 template <class TR, int D>
-__global__ __launch_bounds__(256) void combine_kernel(const Params p) {
+__global__ __launch_bounds__(64) void combine_kernel(const Params p) {
     constexpr float NEG_INF = -__builtin_inff();
-    constexpr int MAXI = 4;  // splits per lane held in registers per pass
-    __shared__ float wts[kMaxSplits];
-    __shared__ float redm[4], redl[4];
-    __shared__ f32x4_t part[4][16];
+    __shared__ __attribute__((aligned(16))) float msh[kMaxSplits], lsh[kMaxSplits], wts[kMaxSplits];
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int S = p.splits;
-    const int cgp = lane & 15, ph = lane >> 4;   // float4 column group, split phase
+    const int lane = threadIdx.x;
+    const int S = p.splits, NPASS = (S + 63) / 64;
+    const int cgp = lane & 15, ph = lane >> 4;
     const int d = blockIdx.y * 64 + 4 * cgp;
     const bool dv = d < D;
     const float* po = p.ws_o + row * S * D + d;
     const float* ml = p.ws_ml + row * S * 2;
-    // first pass of partial loads is issued before anything depends on it
-    f32x4_t v[MAXI];
+    // the first pass's partial loads go out before anything depends on them
+    f32x4_t v[16];
 #pragma unroll
-    for (int i = 0; i < MAXI; ++i) {
-        const int s = 16 * i + 4 * w + ph;
+    for (int i = 0; i < 16; ++i) {
+        const int s = 4 * i + ph;
         v[i] = (dv && s < S) ? *reinterpret_cast<const f32x4_t*>(po + (int64_t)s * D) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    float mreg[kMaxSplits / 256], lreg[kMaxSplits / 256];
     float M = NEG_INF;
-#pragma unroll
-    for (int i = 0; i < kMaxSplits / 256; ++i) {
-        const int s = tid + 256 * i;
-        mreg[i] = s < S ? ml[2 * s] : NEG_INF;
-        lreg[i] = s < S ? ml[2 * s + 1] : 0.f;
-        M = fmaxf(M, mreg[i]);
+    for (int k = 0; k < NPASS; ++k) {
+        const int s = 64 * k + lane;
+        const float m = s < S ? ml[2 * s] : NEG_INF, l = s < S ? ml[2 * s + 1] : 0.f;
+        msh[s] = m;
+        lsh[s] = l;
+        M = fmaxf(M, m);
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    if (lane == 0) redm[w] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
+    for (int o = 1; o < 16; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    M = max_x32(max_x16(M));
     float den = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxSplits / 256; ++i) {
-        const int s = tid + 256 * i;
-        const float wv = (mreg[i] == NEG_INF || M == NEG_INF) ? 0.f : fast_exp2(mreg[i] - M);
-        if (s < S) wts[s] = wv;
-        den = __builtin_fmaf(wv, lreg[i], den);
+    for (int k = 0; k < NPASS; ++k) {
+        const int s = 64 * k + lane;
+        const float m = msh[s];
+        const float w = (m == NEG_INF || M == NEG_INF) ? 0.f : fast_exp2(m - M);
+        den = __builtin_fmaf(w, lsh[s], den);
+        wts[64 * k + 16 * (lane & 3) + (lane >> 2)] = w;  // phase-major within the pass
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
-    if (lane == 0) redl[w] = den;
-    __syncthreads();
-    den = (redl[0] + redl[1]) + (redl[2] + redl[3]);
-
+    for (int o = 1; o < 16; o <<= 1) den += __shfl_xor(den, o, 64);
+    den = sum_x32(sum_x16(den));
+    __syncthreads();  // one wave: orders the weight stores before the reads
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < S; s0 += 16 * MAXI) {
-        if (s0 > 0) {
+    for (int k = 0; k < NPASS; ++k) {
+        if (k > 0) {
 #pragma unroll
-            for (int i = 0; i < MAXI; ++i) {
-                const int s = s0 + 16 * i + 4 * w + ph;
+            for (int i = 0; i < 16; ++i) {
+                const int s = 64 * k + 4 * i + ph;
                 v[i] = (dv && s < S) ? *reinterpret_cast<const f32x4_t*>(po + (int64_t)s * D)
                                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
         }
+        const f32x4_t* wp = reinterpret_cast<const f32x4_t*>(wts + 64 * k + 16 * ph);
 #pragma unroll
-        for (int i = 0; i < MAXI; ++i) {
-            const int s = s0 + 16 * i + 4 * w + ph;
-            const float wv = s < S ? wts[s] : 0.f;
-            acc += wv * v[i];
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4_t w4 = wp[i4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc += w4[j] * v[4 * i4 + j];
         }
     }
-    // sum the 4 split phases of the wave (lanes 16 apart), then the 4 waves
+    // the 4 split phases of a column group: lanes l, l ^ 16, l ^ 32, l ^ 48
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        acc[k] += __shfl_xor(acc[k], 16, 64);
-        acc[k] += __shfl_xor(acc[k], 32, 64);
-    }
-    if (ph == 0) part[w][cgp] = acc;
-    __syncthreads();
-    if (w != 0 || ph != 0 || !dv) return;
-    const f32x4_t tot = (part[0][cgp] + part[1][cgp]) + (part[2][cgp] + part[3][cgp]);
+    for (int k = 0; k < 4; ++k) acc[k] = sum_x32(sum_x16(acc[k]));
+    if (ph != 0 || !dv) return;
     const float inv = (M != NEG_INF && den > 0.f) ? 1.f / den : 0.f;
     const int qi = (int)(row % p.Lq);
     const int64_t bh = row / p.Lq;
     const int qh = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
     char* dst = reinterpret_cast<char*>(p.o) +
                 ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2] + d) * TR::ES;
-    TR::store4(dst, tot * inv);
+    TR::store4(dst, acc * inv);
 }
 
 }  // namespace sdpa_dev
