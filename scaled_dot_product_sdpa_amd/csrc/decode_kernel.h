@@ -19,7 +19,9 @@
 //      V is stored transposed in LDS ([d][key], 4-key x 8-column register
 //      transposes on the way in), so each A operand is one 16-byte read.
 // The workgroup writes its unnormalised partial output, running max (log2
-// domain) and sum; combine_kernel merges the splits.
+// domain) and sum; combine_kernel merges the splits.  With a single split
+// (enough batch x kv-head groups to fill the chip) it writes the output itself
+// and no combine runs.
 #pragma once
 
 #include "attn_common.h"
@@ -253,6 +255,23 @@ __global__ __launch_bounds__(C::NT) void decode_split_kernel(const Params p) {
         __syncthreads();  // Vt / Ps / red are rewritten by the next chunk
     }
 
+    // ---- one split: this workgroup saw every key of its rows; normalise and
+    // store the output (what the merge of a single split computes) ----
+    if (p.splits == 1) {
+        if (rv) {
+            const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+            char* orow = reinterpret_cast<char*>(p.o) +
+                         ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2]) * 2;
+#pragma unroll
+            for (int i = 0; i < C::NDBW; ++i) {
+                const int db = w + NW * i;
+                if (db >= C::NDB) break;
+                const int d = 16 * db + 4 * g;
+                if (d < DO) TR::store4(orow + d * 2, oacc[i] * inv);
+            }
+        }
+        return;
+    }
     // ---- partial state of this split ----
     if (rv) {
         const int64_t row = ((int64_t)b * p.Hq + qh) * p.Lq + qi;

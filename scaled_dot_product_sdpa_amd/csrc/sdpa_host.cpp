@@ -555,10 +555,13 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     st = hip_status(f(p, grid, s));
     if (st != SDPA_OK) return reject(st);
     mark(1);
-    dim3 cgrid((unsigned)rows, (unsigned)((v_head_dim + 63) / 64), 1);
-    st = hip_status(ks->combine(p, cgrid, s));
-    if (st != SDPA_OK) return reject(st);
-    mark(2);
+    // a single split of the 16-bit kernel writes the output itself
+    if (!(plan.splits == 1 && dtype != SDPA_F32)) {
+        dim3 cgrid((unsigned)rows, (unsigned)((v_head_dim + 63) / 64), 1);
+        st = hip_status(ks->combine(p, cgrid, s));
+        if (st != SDPA_OK) return reject(st);
+        mark(2);
+    }
     g_counters[2].fetch_add(1, std::memory_order_relaxed);
     return SDPA_OK;
 }

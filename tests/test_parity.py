@@ -225,3 +225,23 @@ def test_mask_layouts_without_vector_loads(gpu_lib, D, lq, mask_kind, layout):
     out = gpu_lib.forward(q, k, v, scale=c.scale, mask=dm, mask_kind=mask_kind)
     torch.cuda.synchronize()
     assert_parity(out, oracle_out(c), "bf16", f"mask layout {layout} {mask_kind} D={D} Lq={lq}")
+
+
+# --------------------------------------------------------------------------
+# Single split: the decode kernel writes the output itself (no combine), when
+# the batch x kv heads fill the chip or when forced.
+# --------------------------------------------------------------------------
+def test_decode_single_split_from_batch(gpu_lib):
+    route = gpu_lib.describe_route(64, 1, 512, 16, 8, 128, torch.bfloat16, "additive")
+    assert "splits=1 " in route, route
+    c = si.make_case(64, 16, 8, 1, 512, 128, dtype="bf16", layout="blhd", mask_kind="additive", seed=31)
+    assert_parity(run_gpu(c), oracle_out(c), "bf16", "decode B=64 single split")
+
+
+@pytest.mark.parametrize("mask_kind", ["none", "causal", "boolean", "sliding"])
+@pytest.mark.parametrize("D,dv", [(64, None), (128, None), (256, None), (512, None), (192, 128)])
+def test_decode_forced_single_split(gpu_lib, monkeypatch, D, dv, mask_kind):
+    monkeypatch.setenv("SDPA_DECODE_SPLITS", "1")
+    c = si.make_case(1, 8, 2, 3, 900, D, dtype="bf16", layout="bhld", mask_kind=mask_kind, seed=D + 3, dv=dv,
+                     mask_shape="qk", mask_p=0.3, window=50 if mask_kind == "sliding" else None)
+    assert_parity(run_gpu(c), oracle_out(c), "bf16", f"decode single split D={D} {mask_kind}")
