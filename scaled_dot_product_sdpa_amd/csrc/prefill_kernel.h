@@ -5,13 +5,18 @@
 // softmax in base 2, XCD-aware longest-first grid), with the data path
 // rebuilt around two gfx950 features:
 //   * K and V tiles move global -> LDS with buffer_load_dwordx4 ... lds: each
-//     lane of a load writes its 16 bytes at LDS base + 16 * lane, so a tile is
-//     stored row-major with rows of KC + 1 sixteen-byte chunks (KC = D / 8).
-//     The extra chunk is never loaded: it staggers rows over the LDS banks
-//     and holds constants (zeros for K; for V, a one at column D when D is
-//     not a multiple of 32, so the P V product also yields the softmax row
-//     sums).  Two stages are double-buffered: the loads of tile t + 1 fly
-//     while tile t is computed, with one barrier per tile.
+//     lane of a load writes its 16 bytes at LDS base + 16 * lane, and the
+//     global chunk a lane fetches decides the layout.  A tile is stored
+//     row-major.  Below D = 128 a row holds KC + 1 sixteen-byte chunks
+//     (KC = D / 8); the extra chunk is never loaded: it staggers rows over the
+//     LDS banks and holds constants (zeros for K; for V, a one at column D
+//     when D is not a multiple of 32, so the P V product also yields the
+//     softmax row sums).  At D = 128 rows are 256 bytes with chunk c of row r
+//     in slot c ^ sw(r), which puts a 128-bit K read pass (16 lanes: 16
+//     consecutive rows, one chunk) and a transposed 64-bit V read pass (32
+//     lanes: 4 consecutive rows, 4 consecutive chunks) on 64 distinct banks.
+//     Two stages are double-buffered: the loads of tile t + 1 fly while tile
+//     t is computed, with one barrier per tile.
 //   * The A operand of P V (V^T: one head-dim column, eight keys per lane)
 //     comes straight from the row-major V tile through ds_read_b64_tr_b16:
 //     in each 16-lane group, source lane 4 e + j names the 4 columns
@@ -32,7 +37,8 @@ struct PfCfg {
     static constexpr int D = D_, BN = BN_, WM = WM_, OCC = OCC_;
     static constexpr int NT = 64 * WM, BM = 32 * WM;
     static constexpr int KC = D / 8;                  // 16-byte chunks per row
-    static constexpr int RC = KC + 1;                 // chunks per LDS row (one spare)
+    static constexpr bool SWZ = (KC == 16);           // swizzled 256-byte rows, no spare chunk
+    static constexpr int RC = SWZ ? KC : KC + 1;      // 16-byte slots per LDS row
     static constexpr int ROWB = RC * 16;              // bytes per LDS row
     static constexpr int TILEB = BN * ROWB;           // bytes per K or V tile
     static constexpr int NCH = (D + 15) / 16;         // Q K^T chunks (16 head-dim columns)
@@ -41,11 +47,20 @@ struct PfCfg {
     static constexpr bool ONES = (D % 32) != 0;
     static constexpr int SLOTS = BN * RC;             // 16-byte slots per tile
     static constexpr int NLD = (SLOTS + NT - 1) / NT; // load instructions per thread per tile (K or V)
-    static constexpr int LDS = 4 * TILEB + 64;        // K0, V0, K1, V1 (+ slack read past the last row)
+    // K0, V0, K1, V1; padded rows: transposed V reads of the last row may run
+    // up to 32 bytes past it (head-dim columns beyond D, never stored)
+    static constexpr int LDS = 4 * TILEB + (SWZ ? 0 : 64);
     static_assert(D % 8 == 0 && D <= 128, "head dim");
     static_assert(BN % 32 == 0, "key tile");
     static_assert(!ONES || (D % 32) <= 16, "ones column must sit in the spare chunk");
     static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(!SWZ || !ONES, "swizzled rows have no spare chunk");
+    // slot of chunk c in row r: a bijection of 16 consecutive rows onto the 16
+    // slots, and 4 consecutive rows on the 4 groups of 4 slots (64 bytes)
+    static __device__ __forceinline__ int sw(int r) {
+        if constexpr (SWZ) return ((r & 3) << 2) | ((r >> 2) & 3);
+        else return 0;
+    }
 };
 
 template <bool B> struct PfTag { static constexpr bool value = B; };
@@ -148,6 +163,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     }
 
     // ---- spare chunks: K rows 0, V rows (1 at column D if ONES, else 0) ----
+    if constexpr (!C::SWZ)
     for (int r = tid; r < 4 * BN; r += C::NT) {
         const int tile = r / BN, row = r % BN;  // tiles K0, V0, K1, V1
         const bool is_v = tile & 1;
@@ -156,13 +172,13 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         *reinterpret_cast<u32x4_t*>(smem + tile * C::TILEB + row * C::ROWB + C::KC * 16) = z;
     }
 
-    // ---- load slots: lane slot s -> (row, chunk); the spare chunk is never loaded ----
+    // ---- load slots: lane slot s -> (row, chunk); a spare chunk is never loaded ----
     uint32_t kofs[C::NLD], vofs[C::NLD];
     bool sok[C::NLD];
 #pragma unroll
     for (int u = 0; u < C::NLD; ++u) {
         const int s = (u * C::WM + wm) * 64 + lane;  // this lane's 16-byte slot of the tile
-        const int row = s / C::RC, ch = s % C::RC;
+        const int row = s / C::RC, ch = (s % C::RC) ^ C::sw(row);
         sok[u] = (s < C::SLOTS) && (ch < C::KC);
         kofs[u] = (uint32_t)row * kstep32 + (uint32_t)(ch * 16);
         vofs[u] = (uint32_t)row * vstep32 + (uint32_t)(ch * 16);
@@ -221,6 +237,24 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16_t{};
     const float c_scale = p.scale_log2 == 0.f ? 1.f : __builtin_fabsf(p.scale_log2);
 
+    // per-lane LDS read offsets (loop invariant; the swizzle depends on the
+    // row's low 4 bits only, so 32-row and 16-row steps are immediates).
+    // K: row col, chunk 2 ch + hh.  V (transposed reads): key rows
+    // 4 (grp / 2) + e4 (+ 8 for the second read), head-dim columns
+    // 32 db + 16 (grp & 1) + 4 j4 .. + 3, i.e. chunk 4 db + 2 (grp & 1) + j4 / 2, half j4 & 1.
+    const int grp = lane >> 4, s16 = lane & 15;
+    const int e4 = s16 >> 2, j4 = s16 & 3;
+    uint32_t koff[C::NCH], voff[2][C::NDB];
+#pragma unroll
+    for (int ch = 0; ch < C::NCH; ++ch) koff[ch] = (uint32_t)(col * C::ROWB + ((2 * ch + hh) ^ C::sw(col)) * 16);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const int kr = 4 * (grp >> 1) + e4 + 8 * w;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+            voff[w][db] = (uint32_t)(kr * C::ROWB + ((4 * db + 2 * (grp & 1) + (j4 >> 1)) ^ C::sw(kr)) * 16 + 8 * (j4 & 1));
+    }
+
     // S^T of one tile from LDS stage `stage`
     auto scores = [&](int stage, f32x16_t (&sacc)[C::NKB]) {
         const char* kt_lds = smem + (2 * stage) * C::TILEB;
@@ -229,8 +263,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
             sacc[kb] = f32x16_t{};
 #pragma unroll
             for (int ch = 0; ch < C::NCH; ++ch) {
-                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-                    kt_lds + (kb * 32 + col) * C::ROWB + (2 * ch + hh) * 16);
+                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kt_lds + kb * 32 * C::ROWB + koff[ch]);
                 sacc[kb] = TR::mma(a, qf[ch], sacc[kb]);
             }
         }
@@ -262,8 +295,6 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         if constexpr (!C::ONES) l_run += lsum;
         // O^T += V^T P^T; V^T operands via transposed LDS reads of the row-major V tile
         const char* vt_lds = smem + (2 * stage + 1) * C::TILEB;
-        const int grp = lane >> 4, s16 = lane & 15;
-        const int e4 = s16 >> 2, j4 = s16 & 3;
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
@@ -271,13 +302,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
                 u32x4_t bf;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) bf[w] = TR::pack(sacc[kb][8 * pc + 2 * w], sacc[kb][8 * pc + 2 * w + 1]);
-                const int key = kb * 32 + 16 * pc + 4 * (grp >> 1) + e4;
+                const char* vk = vt_lds + (kb * 32 + 16 * pc) * C::ROWB;
 #pragma unroll
                 for (int db = 0; db < C::NDB; ++db) {
-                    const int d = 32 * db + 16 * (grp & 1) + 4 * j4;
-                    const char* a0 = vt_lds + key * C::ROWB + d * 2;
-                    const u32x2_t y0 = lds_read_tr16(a0);
-                    const u32x2_t y1 = lds_read_tr16(a0 + 8 * C::ROWB);
+                    const u32x2_t y0 = lds_read_tr16(vk + voff[0][db]);
+                    const u32x2_t y1 = lds_read_tr16(vk + voff[1][db]);
                     oacc[db] = TR::mma(u32x4_t{y0[0], y0[1], y1[0], y1[1]}, bf, oacc[db]);
                 }
             }
