@@ -201,6 +201,28 @@ def test_zero_and_negative_scale(gpu_lib, D, lq, dtype, mask_kind, scale):
 
 
 # --------------------------------------------------------------------------
+# Scores far from zero: inputs ~ N(0, 4^2), so a row's softmax is nearly one
+# hot and its running max is large (hundreds in base-2 units).  With P rounded
+# to the input type once (relative 2^-9 for bf16) the output may move by a few
+# 2^-9 |V|; the bound below is 2^-7 max|V|.  A path that rounded scaled scores
+# or Q c to 16 bits would err in proportion to the scores instead (it measured
+# 0.5 here against about 0.045).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("mask_kind", ["none", "causal"])
+@pytest.mark.parametrize("D,lq,dtype", [(64, 200, "bf16"), (72, 200, "bf16"), (72, 200, "f16"), (80, 200, "bf16"),
+                                        (96, 200, "bf16"), (128, 200, "bf16"), (256, 120, "bf16"),
+                                        (512, 90, "bf16"), (72, 200, "f32"), (256, 1, "bf16"), (512, 4, "bf16")])
+def test_large_scores(gpu_lib, D, lq, dtype, mask_kind):
+    from gpu_util import errors
+    c = si.make_case(1, 4, 2, lq, 230, D, dtype=dtype, layout="bhld", mask_kind=mask_kind, seed=D + lq, std=4.0)
+    ref = oracle_out(c)
+    max_abs, rel, finite = errors(run_gpu(c), ref)
+    bound = 2.0 ** -7 * float(c.v.abs().max()) if dtype != "f32" else 2e-4
+    msg = f"large scores D={D} Lq={lq} {dtype} {mask_kind}: max_abs={max_abs:.3e} (bound {bound:.3e}) rel_l2={rel:.3e}"
+    assert finite and max_abs <= bound and rel <= 1e-2, msg
+
+
+# --------------------------------------------------------------------------
 # Mask tensors in layouts without the vector fast path: keys strided (a
 # transposed view), rows not a multiple of 4 elements apart, misaligned base.
 # --------------------------------------------------------------------------
