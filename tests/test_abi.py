@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "sdpa.h")
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(sdpa.LIB_PATH):
-        pytest.fail("libsdpa.so is not built (run __graft_entry__.build())")
+        pytest.fail("libsdpa.so is not built (python -m scaled_dot_product_sdpa_amd.build)")
     return sdpa.load()
 
 
