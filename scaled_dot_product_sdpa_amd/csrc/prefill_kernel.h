@@ -45,6 +45,7 @@ struct PfCfg {
     static constexpr int NDB = (D + 31) / 32;         // 32-column O^T blocks
     static constexpr int NKB = BN / 32;               // 32-key score blocks per tile
     static constexpr bool ONES = (D % 32) != 0;
+    static constexpr int LA = 3;                      // operand reads in flight ahead of the MFMAs
     static constexpr int SLOTS = BN * RC;             // 16-byte slots per tile
     static constexpr int NLD = (SLOTS + NT - 1) / NT; // load instructions per thread per tile (K or V)
     // K0, V0, K1, V1; padded rows: transposed V reads of the last row may run
@@ -255,17 +256,26 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
             voff[w][db] = (uint32_t)(kr * C::ROWB + ((4 * db + 2 * (grp & 1) + (j4 >> 1)) ^ C::sw(kr)) * 16 + 8 * (j4 & 1));
     }
 
-    // S^T of one tile from LDS stage `stage`
+    // S^T of one tile from LDS stage `stage`; operand reads run LA products
+    // ahead of their MFMAs (scheduling fences keep them there)
+    constexpr int LA = C::LA;
     auto scores = [&](int stage, f32x16_t (&sacc)[C::NKB]) {
         const char* kt_lds = smem + (2 * stage) * C::TILEB;
+        constexpr int N = C::NKB * C::NCH;
+        auto rd = [&](int i) {
+            return *reinterpret_cast<const u32x4_t*>(kt_lds + (i / C::NCH) * 32 * C::ROWB + koff[i % C::NCH]);
+        };
+        u32x4_t ring[LA];
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
-            sacc[kb] = f32x16_t{};
+        for (int i = 0; i < LA && i < N; ++i) ring[i] = rd(i);
 #pragma unroll
-            for (int ch = 0; ch < C::NCH; ++ch) {
-                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kt_lds + kb * 32 * C::ROWB + koff[ch]);
-                sacc[kb] = TR::mma(a, qf[ch], sacc[kb]);
-            }
+        for (int i = 0; i < N; ++i) {
+            const u32x4_t a = ring[i % LA];
+            if (i + LA < N) ring[i % LA] = rd(i + LA);
+            __builtin_amdgcn_sched_barrier(0);
+            const int kb = i / C::NCH, ch = i % C::NCH;
+            sacc[kb] = TR::mma(a, qf[ch], ch == 0 ? f32x16_t{} : sacc[kb]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     // online softmax on scores already scaled (c_eff = 1) or raw (c_eff = scale)
@@ -295,21 +305,34 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         if constexpr (!C::ONES) l_run += lsum;
         // O^T += V^T P^T; V^T operands via transposed LDS reads of the row-major V tile
         const char* vt_lds = smem + (2 * stage + 1) * C::TILEB;
+        u32x4_t bf[C::NKB][2];
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
+        for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-            for (int pc = 0; pc < 2; ++pc) {
-                u32x4_t bf;
+            for (int pc = 0; pc < 2; ++pc)
 #pragma unroll
-                for (int w = 0; w < 4; ++w) bf[w] = TR::pack(sacc[kb][8 * pc + 2 * w], sacc[kb][8 * pc + 2 * w + 1]);
-                const char* vk = vt_lds + (kb * 32 + 16 * pc) * C::ROWB;
+                for (int w = 0; w < 4; ++w)
+                    bf[kb][pc][w] = TR::pack(sacc[kb][8 * pc + 2 * w], sacc[kb][8 * pc + 2 * w + 1]);
+        // products (kb, pc, db), db fastest; V^T operand reads run LA products ahead
+        constexpr int N = C::NKB * 2 * C::NDB, LAV = C::LA;
+        auto rd = [&](int i) {
+            const int db = i % C::NDB, pc = (i / C::NDB) & 1, kb = i / (2 * C::NDB);
+            const char* vk = vt_lds + (kb * 32 + 16 * pc) * C::ROWB;
+            const u32x2_t y0 = lds_read_tr16(vk + voff[0][db]);
+            const u32x2_t y1 = lds_read_tr16(vk + voff[1][db]);
+            return u32x4_t{y0[0], y0[1], y1[0], y1[1]};
+        };
+        u32x4_t ring[LAV];
 #pragma unroll
-                for (int db = 0; db < C::NDB; ++db) {
-                    const u32x2_t y0 = lds_read_tr16(vk + voff[0][db]);
-                    const u32x2_t y1 = lds_read_tr16(vk + voff[1][db]);
-                    oacc[db] = TR::mma(u32x4_t{y0[0], y0[1], y1[0], y1[1]}, bf, oacc[db]);
-                }
-            }
+        for (int i = 0; i < LAV && i < N; ++i) ring[i] = rd(i);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const u32x4_t a = ring[i % LAV];
+            if (i + LAV < N) ring[i % LAV] = rd(i + LAV);
+            __builtin_amdgcn_sched_barrier(0);
+            const int db = i % C::NDB, pc = (i / C::NDB) & 1, kb = i / (2 * C::NDB);
+            oacc[db] = TR::mma(a, bf[kb][pc], oacc[db]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
