@@ -15,8 +15,11 @@
 //     in slot c ^ sw(r), which puts a 128-bit K read pass (16 lanes: 16
 //     consecutive rows, one chunk) and a transposed 64-bit V read pass (32
 //     lanes: 4 consecutive rows, 4 consecutive chunks) on 64 distinct banks.
-//     Two stages are double-buffered: the loads of tile t + 1 fly while tile
-//     t is computed, with one barrier per tile.
+//     Two stages are double-buffered: the loads of tile t + 1 fly during Q K^T
+//     and the softmax of tile t, with one barrier per tile.  (hipcc waits for
+//     them before tile t's first transposed V read, which it cannot tell apart
+//     from the stage being loaded; one LDS array per stage would avoid that,
+//     but the two loop bodies it needs cost an occupancy step.)
 //   * The A operand of P V (V^T: one head-dim column, eight keys per lane)
 //     comes straight from the row-major V tile through ds_read_b64_tr_b16:
 //     in each 16-lane group, source lane 4 e + j names the 4 columns
