@@ -20,6 +20,7 @@ struct TileInfo {
     int nt;   // threads per workgroup
     int lds;  // bytes of LDS per workgroup
     int heads = 1;  // prefill: query heads of one grouped-query group sharing a workgroup (at most)
+    int causal_pairs = 0;  // prefill, causal mask: a workgroup takes two row tiles (t, last - t)
 };
 
 struct KernelSet {

@@ -49,6 +49,7 @@ struct PfCfg {
     static constexpr int NKB = BN / 32;               // 32-key score blocks per tile
     static constexpr bool ONES = (D % 32) != 0;
     static constexpr int LA = 3;                      // operand reads in flight ahead of the MFMAs
+    static constexpr bool PAIRS = true;               // causal: two row tiles per workgroup (see the kernel)
     static constexpr int SLOTS = BN * RC;             // 16-byte slots per tile
     static constexpr int NLD = (SLOTS + NT - 1) / NT; // load instructions per thread per tile (K or V)
     // K0, V0, K1, V1; padded rows: transposed V reads of the last row may run
@@ -81,8 +82,10 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     const int col = lane & 31, hh = lane >> 5;
 
     // ---- work item (XCD-aware, longest causal tiles first) ----
+    constexpr bool PAIRS = C::PAIRS && MASK == MASK_CAUSAL;
     const int nqt = (p.Lq + BM - 1) / BM;
-    const int total = nqt * p.Hq * p.B;
+    const int nit = PAIRS ? (nqt + 1) / 2 : nqt;  // row-tile items per head
+    const int total = nit * p.Hq * p.B;
     const int per = (total + 7) / 8;
     const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
     if (item >= total) return;
@@ -96,351 +99,364 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         tt = r % nqt;
         b = r / nqt;
     } else {
-        tt = item % nqt;
-        const int bh = item / nqt;
+        tt = item % nit;
+        const int bh = item / nit;
         qh = bh % p.Hq;
         b = bh / p.Hq;
     }
     constexpr bool CAUSAL_END = (MASK == MASK_CAUSAL || MASK == MASK_SLIDE);
-    const int t = CAUSAL_END ? nqt - 1 - tt : tt;
-    const int g = qh / p.n_rep;
-    const int i0 = t * BM;
-    const int qmin = i0 + 32 * wm;  // first query row of this wave
-    const int qi = qmin + col;
-    const bool rv = qi < p.Lq;
-    const int off = p.Lk - p.Lq;
-    int kend = p.Lk;
-    if (CAUSAL_END) {
-        const int64_t e = (int64_t)i0 + BM + off;
-        kend = (int)(e < 0 ? 0 : (e > p.Lk ? p.Lk : e));
-    }
-    const int ntiles = (kend + BN - 1) / BN;
-    // key tiles [t0, ntiles) hold every key some row of this workgroup attends;
-    // tiles [tp0, tp1) need no per-element mask for any row of this wave
-    int t0 = 0;
-    if (MASK == MASK_SLIDE) t0 = min(ntiles, max(0, i0 + off - p.window + 1) / BN);
-    int tp0 = t0, tp1 = kend / BN;
-    if (CAUSAL_END) tp1 = min(tp1, max(0, qmin + off + 1) / BN);
-    if (MASK == MASK_SLIDE) {
-        const int lo = min(qmin + 31, p.Lq - 1) + off - p.window + 1;  // window's left edge, wave's last row
-        tp0 = max(t0, lo <= 0 ? 0 : (lo + BN - 1) / BN);
-    }
-    if (HAS_MT) tp1 = tp0;
-    tp0 = min(tp0, ntiles);
-    tp1 = max(tp0, min(tp1, ntiles));
-
-    // ---- buffer resources over this (batch, kv head)'s K and V rows ----
-    const int64_t kstep = (int64_t)p.ks[2] * 2, vstep = (int64_t)p.vs[2] * 2;
-    const char* kglob = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)g * p.ks[1]) * 2;
-    const char* vglob = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)g * p.vs[1]) * 2;
-    const uint32_t kstep32 = (uint32_t)kstep, vstep32 = (uint32_t)vstep;
-    const __amdgpu_buffer_rsrc_t krs =
-        make_rsrc(kglob, kend > 0 ? (uint32_t)(kend - 1) * kstep32 + (uint32_t)(D * 2) : 0u);
-    const __amdgpu_buffer_rsrc_t vrs =
-        make_rsrc(vglob, kend > 0 ? (uint32_t)(kend - 1) * vstep32 + (uint32_t)(D * 2) : 0u);
-
-    // ---- Q fragments (MFMA B operand), zero beyond D / beyond the rows ----
-    u32x4_t qf[C::NCH];
-    {
-        const char* qrow = reinterpret_cast<const char*>(p.q) +
-                           ((int64_t)b * p.qs[0] + (int64_t)qh * p.qs[1] + (int64_t)qi * p.qs[2]) * 2;
-#pragma unroll
-        for (int ch = 0; ch < C::NCH; ++ch) {
-            const int d = ch * 16 + hh * 8;
-            qf[ch] = (rv && d < D) ? *reinterpret_cast<const u32x4_t*>(qrow + d * 2) : u32x4_t{0u, 0u, 0u, 0u};
+    // the row tiles of one workgroup: one, or with PAIRS (causal) two whose
+    // key ranges add up to the same length for every workgroup (t and nqt - 1 - t),
+    // so no single long row tile outlasts the rest of the grid
+    auto run = [&](const int t) __attribute__((always_inline)) {
+        const int g = qh / p.n_rep;
+        const int i0 = t * BM;
+        const int qmin = i0 + 32 * wm;  // first query row of this wave
+        const int qi = qmin + col;
+        const bool rv = qi < p.Lq;
+        const int off = p.Lk - p.Lq;
+        int kend = p.Lk;
+        if (CAUSAL_END) {
+            const int64_t e = (int64_t)i0 + BM + off;
+            kend = (int)(e < 0 ? 0 : (e > p.Lk ? p.Lk : e));
         }
-        if constexpr (ROPE) {  // rotary embedding of the query row (columns < rope_dim)
-            if (rv)
-                rope_q_fragments<TR, C::NCH, 16>(qf, qrow, hh * 8, p.rope_dim, p.rope_cos, p.rope_sin,
-                                                 (int64_t)p.rope_pos0 + qi);
+        const int ntiles = (kend + BN - 1) / BN;
+        // key tiles [t0, ntiles) hold every key some row of this workgroup attends;
+        // tiles [tp0, tp1) need no per-element mask for any row of this wave
+        int t0 = 0;
+        if (MASK == MASK_SLIDE) t0 = min(ntiles, max(0, i0 + off - p.window + 1) / BN);
+        int tp0 = t0, tp1 = kend / BN;
+        if (CAUSAL_END) tp1 = min(tp1, max(0, qmin + off + 1) / BN);
+        if (MASK == MASK_SLIDE) {
+            const int lo = min(qmin + 31, p.Lq - 1) + off - p.window + 1;  // window's left edge, wave's last row
+            tp0 = max(t0, lo <= 0 ? 0 : (lo + BN - 1) / BN);
         }
-        // a negative scale runs as |scale| on -Q (exact: a sign flip) and a zero
-        // scale as scale 1 on Q = 0 (every score is 0 either way), so the scale
-        // is positive and the row max can always be taken on unscaled scores
-        if (p.scale_log2 < 0.f) {
-#pragma unroll
-            for (int ch = 0; ch < C::NCH; ++ch) qf[ch] ^= 0x80008000u;
-        } else if (p.scale_log2 == 0.f) {
-#pragma unroll
-            for (int ch = 0; ch < C::NCH; ++ch) qf[ch] = u32x4_t{0u, 0u, 0u, 0u};
+        if (HAS_MT) tp1 = tp0;
+        tp0 = min(tp0, ntiles);
+        tp1 = max(tp0, min(tp1, ntiles));
+
+        // ---- buffer resources over this (batch, kv head)'s K and V rows ----
+        const int64_t kstep = (int64_t)p.ks[2] * 2, vstep = (int64_t)p.vs[2] * 2;
+        const char* kglob = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)g * p.ks[1]) * 2;
+        const char* vglob = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)g * p.vs[1]) * 2;
+        const uint32_t kstep32 = (uint32_t)kstep, vstep32 = (uint32_t)vstep;
+        const __amdgpu_buffer_rsrc_t krs =
+            make_rsrc(kglob, kend > 0 ? (uint32_t)(kend - 1) * kstep32 + (uint32_t)(D * 2) : 0u);
+        const __amdgpu_buffer_rsrc_t vrs =
+            make_rsrc(vglob, kend > 0 ? (uint32_t)(kend - 1) * vstep32 + (uint32_t)(D * 2) : 0u);
+
+        // ---- Q fragments (MFMA B operand), zero beyond D / beyond the rows ----
+        u32x4_t qf[C::NCH];
+        {
+            const char* qrow = reinterpret_cast<const char*>(p.q) +
+                               ((int64_t)b * p.qs[0] + (int64_t)qh * p.qs[1] + (int64_t)qi * p.qs[2]) * 2;
+    #pragma unroll
+            for (int ch = 0; ch < C::NCH; ++ch) {
+                const int d = ch * 16 + hh * 8;
+                qf[ch] = (rv && d < D) ? *reinterpret_cast<const u32x4_t*>(qrow + d * 2) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+            if constexpr (ROPE) {  // rotary embedding of the query row (columns < rope_dim)
+                if (rv)
+                    rope_q_fragments<TR, C::NCH, 16>(qf, qrow, hh * 8, p.rope_dim, p.rope_cos, p.rope_sin,
+                                                     (int64_t)p.rope_pos0 + qi);
+            }
+            // a negative scale runs as |scale| on -Q (exact: a sign flip) and a zero
+            // scale as scale 1 on Q = 0 (every score is 0 either way), so the scale
+            // is positive and the row max can always be taken on unscaled scores
+            if (p.scale_log2 < 0.f) {
+    #pragma unroll
+                for (int ch = 0; ch < C::NCH; ++ch) qf[ch] ^= 0x80008000u;
+            } else if (p.scale_log2 == 0.f) {
+    #pragma unroll
+                for (int ch = 0; ch < C::NCH; ++ch) qf[ch] = u32x4_t{0u, 0u, 0u, 0u};
+            }
         }
-    }
 
-    // ---- spare chunks: K rows 0, V rows (1 at column D if ONES, else 0) ----
-    if constexpr (!C::SWZ)
-    for (int r = tid; r < 4 * BN; r += C::NT) {
-        const int tile = r / BN, row = r % BN;  // tiles K0, V0, K1, V1
-        const bool is_v = tile & 1;
-        u32x4_t z = {0u, 0u, 0u, 0u};
-        if (is_v && C::ONES) z[0] = OneBits<TR>::v;
-        *reinterpret_cast<u32x4_t*>(smem + tile * C::TILEB + row * C::ROWB + C::KC * 16) = z;
-    }
+        // ---- spare chunks: K rows 0, V rows (1 at column D if ONES, else 0) ----
+        if constexpr (!C::SWZ)
+        for (int r = tid; r < 4 * BN; r += C::NT) {
+            const int tile = r / BN, row = r % BN;  // tiles K0, V0, K1, V1
+            const bool is_v = tile & 1;
+            u32x4_t z = {0u, 0u, 0u, 0u};
+            if (is_v && C::ONES) z[0] = OneBits<TR>::v;
+            *reinterpret_cast<u32x4_t*>(smem + tile * C::TILEB + row * C::ROWB + C::KC * 16) = z;
+        }
 
-    // ---- load slots: lane slot s -> (row, chunk); a spare chunk is never loaded ----
-    uint32_t kofs[C::NLD], vofs[C::NLD];
-    bool sok[C::NLD];
-#pragma unroll
-    for (int u = 0; u < C::NLD; ++u) {
-        const int s = (u * C::WM + wm) * 64 + lane;  // this lane's 16-byte slot of the tile
-        const int row = s / C::RC, ch = (s % C::RC) ^ C::sw(row);
-        sok[u] = (s < C::SLOTS) && (ch < C::KC);
-        kofs[u] = (uint32_t)row * kstep32 + (uint32_t)(ch * 16);
-        vofs[u] = (uint32_t)row * vstep32 + (uint32_t)(ch * 16);
-    }
-    auto issue_tile = [&](int kt, int stage) {
-        char* kt_lds = smem + (2 * stage) * C::TILEB;
-        char* vt_lds = smem + (2 * stage + 1) * C::TILEB;
-        const uint32_t kb0 = (uint32_t)kt * kstep32, vb0 = (uint32_t)kt * vstep32;
-#pragma unroll
+        // ---- load slots: lane slot s -> (row, chunk); a spare chunk is never loaded ----
+        uint32_t kofs[C::NLD], vofs[C::NLD];
+        bool sok[C::NLD];
+    #pragma unroll
         for (int u = 0; u < C::NLD; ++u) {
-            const int blk = (u * C::WM + wm) * 64 * 16;  // LDS byte offset of this instruction's 64 slots
-            if (blk >= C::SLOTS * 16) break;
-            if (sok[u]) {
-                buffer_load16_lds(krs, kt_lds + blk, kofs[u] + kb0);
-                buffer_load16_lds(vrs, vt_lds + blk, vofs[u] + vb0);
-            }
+            const int s = (u * C::WM + wm) * 64 + lane;  // this lane's 16-byte slot of the tile
+            const int row = s / C::RC, ch = (s % C::RC) ^ C::sw(row);
+            sok[u] = (s < C::SLOTS) && (ch < C::KC);
+            kofs[u] = (uint32_t)row * kstep32 + (uint32_t)(ch * 16);
+            vofs[u] = (uint32_t)row * vstep32 + (uint32_t)(ch * 16);
         }
-    };
-
-    // mask rows: rows past Lq read row Lq - 1 (never stored).  One buffer
-    // resource per wave starts at the wave's first row and ends at the mask's
-    // last byte (32-bit element offsets within it: checked on the host), so
-    // every group is one branch-free vector load (or four scalar ones).
-    constexpr int MES = MASK == MASK_BOOL ? 1 : (MASK == MASK_ADD16 ? 2 : 4);
-    const int q0c = min(qmin, p.Lq - 1), qic = min(qi, p.Lq - 1);
-    const int64_t mbase = HAS_MT ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)q0c * p.ms[2] : 0;
-    const uint32_t mlane = HAS_MT ? (uint32_t)((qic - q0c) * p.ms[2]) : 0u;
-    const int64_t mleft = HAS_MT ? p.mask_span - mbase * MES : 0;
-    const __amdgpu_buffer_rsrc_t mrs =
-        make_rsrc(HAS_MT ? reinterpret_cast<const char*>(p.mask) + mbase * MES : nullptr,
-                  (uint32_t)(mleft > 0xffffffffLL ? 0xffffffffLL : mleft));
-    typename MaskRaw<MASK>::type mr[HAS_MT ? C::NKB : 1][4];
-    auto load_mask = [&](int kt) {
-        if constexpr (HAS_MT) {
-            if (p.mask_vec) {
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                    for (int a4 = 0; a4 < 4; ++a4)
-                        mr[kb][a4] = load_mask_group_rs<MASK>(
-                            mrs, (mlane + (uint32_t)(kt + kb * 32 + 8 * a4 + 4 * hh)) * MES);
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                    for (int a4 = 0; a4 < 4; ++a4)
-                        mr[kb][a4] = load_mask_group_rs_strided<MASK>(mrs, mlane, kt + kb * 32 + 8 * a4 + 4 * hh,
-                                                                      (uint32_t)p.ms[3]);
+        auto issue_tile = [&](int kt, int stage) {
+            char* kt_lds = smem + (2 * stage) * C::TILEB;
+            char* vt_lds = smem + (2 * stage + 1) * C::TILEB;
+            const uint32_t kb0 = (uint32_t)kt * kstep32, vb0 = (uint32_t)kt * vstep32;
+    #pragma unroll
+            for (int u = 0; u < C::NLD; ++u) {
+                const int blk = (u * C::WM + wm) * 64 * 16;  // LDS byte offset of this instruction's 64 slots
+                if (blk >= C::SLOTS * 16) break;
+                if (sok[u]) {
+                    buffer_load16_lds(krs, kt_lds + blk, kofs[u] + kb0);
+                    buffer_load16_lds(vrs, vt_lds + blk, vofs[u] + vb0);
+                }
             }
-        }
-    };
-
-    float m_run = NEG_INF, l_run = 0.f;
-    f32x16_t oacc[C::NDB];
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16_t{};
-    const float c_scale = p.scale_log2 == 0.f ? 1.f : __builtin_fabsf(p.scale_log2);
-
-    // per-lane LDS read offsets (loop invariant; the swizzle depends on the
-    // row's low 4 bits only, so 32-row and 16-row steps are immediates).
-    // K: row col, chunk 2 ch + hh.  V (transposed reads): key rows
-    // 4 (grp / 2) + e4 (+ 8 for the second read), head-dim columns
-    // 32 db + 16 (grp & 1) + 4 j4 .. + 3, i.e. chunk 4 db + 2 (grp & 1) + j4 / 2, half j4 & 1.
-    const int grp = lane >> 4, s16 = lane & 15;
-    const int e4 = s16 >> 2, j4 = s16 & 3;
-    uint32_t koff[C::NCH], voff[2][C::NDB];
-#pragma unroll
-    for (int ch = 0; ch < C::NCH; ++ch) koff[ch] = (uint32_t)(col * C::ROWB + ((2 * ch + hh) ^ C::sw(col)) * 16);
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        const int kr = 4 * (grp >> 1) + e4 + 8 * w;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-            voff[w][db] = (uint32_t)(kr * C::ROWB + ((4 * db + 2 * (grp & 1) + (j4 >> 1)) ^ C::sw(kr)) * 16 + 8 * (j4 & 1));
-    }
-
-    // S^T of one tile from LDS stage `stage`; operand reads run LA products
-    // ahead of their MFMAs (scheduling fences keep them there)
-    constexpr int LA = C::LA;
-    auto scores = [&](int stage, f32x16_t (&sacc)[C::NKB]) {
-        const char* kt_lds = smem + (2 * stage) * C::TILEB;
-        constexpr int N = C::NKB * C::NCH;
-        auto rd = [&](int i) {
-            return *reinterpret_cast<const u32x4_t*>(kt_lds + (i / C::NCH) * 32 * C::ROWB + koff[i % C::NCH]);
         };
-        u32x4_t ring[LA];
-#pragma unroll
-        for (int i = 0; i < LA && i < N; ++i) ring[i] = rd(i);
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const u32x4_t a = ring[i % LA];
-            if (i + LA < N) ring[i % LA] = rd(i + LA);
-            __builtin_amdgcn_sched_barrier(0);
-            const int kb = i / C::NCH, ch = i % C::NCH;
-            sacc[kb] = TR::mma(a, qf[ch], ch == 0 ? f32x16_t{} : sacc[kb]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    // online softmax on scores already scaled (c_eff = 1) or raw (c_eff = scale)
-    auto softmax_pv = [&](int stage, f32x16_t (&sacc)[C::NKB], float mtile, float c_eff) {
-        mtile = max_x32(mtile);
-        if (__any(mtile > m_run + kRescale)) {
-            const float m_new = fmaxf(m_run, mtile);
-            const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-            asm volatile("");  // keep this a branch, not a select on every tile
-#pragma unroll
+
+        // mask rows: rows past Lq read row Lq - 1 (never stored).  One buffer
+        // resource per wave starts at the wave's first row and ends at the mask's
+        // last byte (32-bit element offsets within it: checked on the host), so
+        // every group is one branch-free vector load (or four scalar ones).
+        constexpr int MES = MASK == MASK_BOOL ? 1 : (MASK == MASK_ADD16 ? 2 : 4);
+        const int q0c = min(qmin, p.Lq - 1), qic = min(qi, p.Lq - 1);
+        const int64_t mbase = HAS_MT ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)q0c * p.ms[2] : 0;
+        const uint32_t mlane = HAS_MT ? (uint32_t)((qic - q0c) * p.ms[2]) : 0u;
+        const int64_t mleft = HAS_MT ? p.mask_span - mbase * MES : 0;
+        const __amdgpu_buffer_rsrc_t mrs =
+            make_rsrc(HAS_MT ? reinterpret_cast<const char*>(p.mask) + mbase * MES : nullptr,
+                      (uint32_t)(mleft > 0xffffffffLL ? 0xffffffffLL : mleft));
+        typename MaskRaw<MASK>::type mr[HAS_MT ? C::NKB : 1][4];
+        auto load_mask = [&](int kt) {
+            if constexpr (HAS_MT) {
+                if (p.mask_vec) {
+    #pragma unroll
+                    for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                        for (int a4 = 0; a4 < 4; ++a4)
+                            mr[kb][a4] = load_mask_group_rs<MASK>(
+                                mrs, (mlane + (uint32_t)(kt + kb * 32 + 8 * a4 + 4 * hh)) * MES);
+                } else {
+    #pragma unroll
+                    for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                        for (int a4 = 0; a4 < 4; ++a4)
+                            mr[kb][a4] = load_mask_group_rs_strided<MASK>(mrs, mlane, kt + kb * 32 + 8 * a4 + 4 * hh,
+                                                                          (uint32_t)p.ms[3]);
+                }
+            }
+        };
+
+        float m_run = NEG_INF, l_run = 0.f;
+        f32x16_t oacc[C::NDB];
+    #pragma unroll
+        for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16_t{};
+        const float c_scale = p.scale_log2 == 0.f ? 1.f : __builtin_fabsf(p.scale_log2);
+
+        // per-lane LDS read offsets (loop invariant; the swizzle depends on the
+        // row's low 4 bits only, so 32-row and 16-row steps are immediates).
+        // K: row col, chunk 2 ch + hh.  V (transposed reads): key rows
+        // 4 (grp / 2) + e4 (+ 8 for the second read), head-dim columns
+        // 32 db + 16 (grp & 1) + 4 j4 .. + 3, i.e. chunk 4 db + 2 (grp & 1) + j4 / 2, half j4 & 1.
+        const int grp = lane >> 4, s16 = lane & 15;
+        const int e4 = s16 >> 2, j4 = s16 & 3;
+        uint32_t koff[C::NCH], voff[2][C::NDB];
+    #pragma unroll
+        for (int ch = 0; ch < C::NCH; ++ch) koff[ch] = (uint32_t)(col * C::ROWB + ((2 * ch + hh) ^ C::sw(col)) * 16);
+    #pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const int kr = 4 * (grp >> 1) + e4 + 8 * w;
+    #pragma unroll
             for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                voff[w][db] = (uint32_t)(kr * C::ROWB + ((4 * db + 2 * (grp & 1) + (j4 >> 1)) ^ C::sw(kr)) * 16 + 8 * (j4 & 1));
         }
-        const float muse = (m_run == NEG_INF) ? 0.f : m_run;
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = fast_exp2(__builtin_fmaf(sacc[kb][r], c_eff, -muse));
-                sacc[kb][r] = e;
-                lsum += e;
-            }
-        if constexpr (!C::ONES) l_run += lsum;
-        // O^T += V^T P^T; V^T operands via transposed LDS reads of the row-major V tile
-        const char* vt_lds = smem + (2 * stage + 1) * C::TILEB;
-        u32x4_t bf[C::NKB][2];
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-            for (int pc = 0; pc < 2; ++pc)
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    bf[kb][pc][w] = TR::pack(sacc[kb][8 * pc + 2 * w], sacc[kb][8 * pc + 2 * w + 1]);
-        // products (kb, pc, db), db fastest; V^T operand reads run LA products ahead
-        constexpr int N = C::NKB * 2 * C::NDB, LAV = C::LA;
-        auto rd = [&](int i) {
-            const int db = i % C::NDB, pc = (i / C::NDB) & 1, kb = i / (2 * C::NDB);
-            const char* vk = vt_lds + (kb * 32 + 16 * pc) * C::ROWB;
-            const u32x2_t y0 = lds_read_tr16(vk + voff[0][db]);
-            const u32x2_t y1 = lds_read_tr16(vk + voff[1][db]);
-            return u32x4_t{y0[0], y0[1], y1[0], y1[1]};
-        };
-        u32x4_t ring[LAV];
-#pragma unroll
-        for (int i = 0; i < LAV && i < N; ++i) ring[i] = rd(i);
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const u32x4_t a = ring[i % LAV];
-            if (i + LAV < N) ring[i % LAV] = rd(i + LAV);
-            __builtin_amdgcn_sched_barrier(0);
-            const int db = i % C::NDB, pc = (i / C::NDB) & 1, kb = i / (2 * C::NDB);
-            oacc[db] = TR::mma(a, bf[kb][pc], oacc[db]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
 
-    // one key tile; the mask-free and the masked variants run as separate loops
-    // so neither carries the other's code (or register copies) around its body.
-    // TAIL: the last tile of a mask-free or mask-tensor workgroup, whose keys
-    // may run past the end (causal and sliding masks exclude them already).
-    auto tile = [&](int it, auto masked_tag, auto tail_tag) __attribute__((always_inline)) {
-        constexpr bool MASKED = decltype(masked_tag)::value, TAIL = decltype(tail_tag)::value;
-        const int kt = it * BN, stage = it & 1;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // tile `it` is in LDS; every wave is done with the other stage
-        if (it + 1 < ntiles) issue_tile(kt + BN, stage ^ 1);
-        f32x16_t sacc[C::NKB];
-        scores(stage, sacc);
-        if constexpr (!MASKED) {
-            // no per-element mask: row max on unscaled scores
-            float mx = NEG_INF;
-#pragma unroll
+        // S^T of one tile from LDS stage `stage`; operand reads run LA products
+        // ahead of their MFMAs (scheduling fences keep them there)
+        constexpr int LA = C::LA;
+        auto scores = [&](int stage, f32x16_t (&sacc)[C::NKB]) {
+            const char* kt_lds = smem + (2 * stage) * C::TILEB;
+            constexpr int N = C::NKB * C::NCH;
+            auto rd = [&](int i) {
+                return *reinterpret_cast<const u32x4_t*>(kt_lds + (i / C::NCH) * 32 * C::ROWB + koff[i % C::NCH]);
+            };
+            u32x4_t ring[LA];
+    #pragma unroll
+            for (int i = 0; i < LA && i < N; ++i) ring[i] = rd(i);
+    #pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const u32x4_t a = ring[i % LA];
+                if (i + LA < N) ring[i % LA] = rd(i + LA);
+                __builtin_amdgcn_sched_barrier(0);
+                const int kb = i / C::NCH, ch = i % C::NCH;
+                sacc[kb] = TR::mma(a, qf[ch], ch == 0 ? f32x16_t{} : sacc[kb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // online softmax on scores already scaled (c_eff = 1) or raw (c_eff = scale)
+        auto softmax_pv = [&](int stage, f32x16_t (&sacc)[C::NKB], float mtile, float c_eff) {
+            mtile = max_x32(mtile);
+            if (__any(mtile > m_run + kRescale)) {
+                const float m_new = fmaxf(m_run, mtile);
+                const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+                asm volatile("");  // keep this a branch, not a select on every tile
+    #pragma unroll
+                for (int db = 0; db < C::NDB; ++db)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+            const float muse = (m_run == NEG_INF) ? 0.f : m_run;
+            float lsum = 0.f;
+    #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            softmax_pv(stage, sacc, mx * c_scale, c_scale);
-        } else {
-            constexpr bool ADD = (MASK == MASK_ADD16 || MASK == MASK_ADD32);
-            // per-element mask; RAW: on unscaled scores (the scale is positive,
-            // so a masked -inf stays -inf once scaled); additive masks add to
-            // scaled scores
-            auto mask_scores = [&](auto raw_tag) __attribute__((always_inline)) {
-                constexpr bool RAW = decltype(raw_tag)::value;
-                float mtile = NEG_INF;
-#pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb) {
-#pragma unroll
-                    for (int a4 = 0; a4 < 4; ++a4) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = kt + kb * 32 + 8 * a4 + 4 * hh + r;
-                            float x = sacc[kb][4 * a4 + r];
-                            if constexpr (!RAW) x *= c_scale;
-                            bool ok = true;
-                            if constexpr (TAIL) ok = j < kend;
-                            if constexpr (ADD)
-                                x = __builtin_fmaf(mask_value<MASK>(mr[kb][a4], r, p.mask_dtype), kLog2e, x);
-                            if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
-                            if constexpr (MASK == MASK_SLIDE) ok = ok && in_window(j, qi + off, p.window);
-                            if constexpr (MASK == MASK_BOOL) ok = ok && ((mr[kb][a4] >> (8 * r)) & 0xffu) != 0u;
-                            x = ok ? x : NEG_INF;
-                            sacc[kb][4 * a4 + r] = x;
-                            mtile = fmaxf(mtile, x);
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float e = fast_exp2(__builtin_fmaf(sacc[kb][r], c_eff, -muse));
+                    sacc[kb][r] = e;
+                    lsum += e;
+                }
+            if constexpr (!C::ONES) l_run += lsum;
+            // O^T += V^T P^T; V^T operands via transposed LDS reads of the row-major V tile
+            const char* vt_lds = smem + (2 * stage + 1) * C::TILEB;
+            u32x4_t bf[C::NKB][2];
+    #pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                for (int pc = 0; pc < 2; ++pc)
+    #pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        bf[kb][pc][w] = TR::pack(sacc[kb][8 * pc + 2 * w], sacc[kb][8 * pc + 2 * w + 1]);
+            // products (kb, pc, db), db fastest; V^T operand reads run LA products ahead
+            constexpr int N = C::NKB * 2 * C::NDB, LAV = C::LA;
+            auto rd = [&](int i) {
+                const int db = i % C::NDB, pc = (i / C::NDB) & 1, kb = i / (2 * C::NDB);
+                const char* vk = vt_lds + (kb * 32 + 16 * pc) * C::ROWB;
+                const u32x2_t y0 = lds_read_tr16(vk + voff[0][db]);
+                const u32x2_t y1 = lds_read_tr16(vk + voff[1][db]);
+                return u32x4_t{y0[0], y0[1], y1[0], y1[1]};
+            };
+            u32x4_t ring[LAV];
+    #pragma unroll
+            for (int i = 0; i < LAV && i < N; ++i) ring[i] = rd(i);
+    #pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const u32x4_t a = ring[i % LAV];
+                if (i + LAV < N) ring[i % LAV] = rd(i + LAV);
+                __builtin_amdgcn_sched_barrier(0);
+                const int db = i % C::NDB, pc = (i / C::NDB) & 1, kb = i / (2 * C::NDB);
+                oacc[db] = TR::mma(a, bf[kb][pc], oacc[db]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        // one key tile; the mask-free and the masked variants run as separate loops
+        // so neither carries the other's code (or register copies) around its body.
+        // TAIL: the last tile of a mask-free or mask-tensor workgroup, whose keys
+        // may run past the end (causal and sliding masks exclude them already).
+        auto tile = [&](int it, auto masked_tag, auto tail_tag) __attribute__((always_inline)) {
+            constexpr bool MASKED = decltype(masked_tag)::value, TAIL = decltype(tail_tag)::value;
+            const int kt = it * BN, stage = it & 1;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();  // tile `it` is in LDS; every wave is done with the other stage
+            if (it + 1 < ntiles) issue_tile(kt + BN, stage ^ 1);
+            f32x16_t sacc[C::NKB];
+            scores(stage, sacc);
+            if constexpr (!MASKED) {
+                // no per-element mask: row max on unscaled scores
+                float mx = NEG_INF;
+    #pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+                softmax_pv(stage, sacc, mx * c_scale, c_scale);
+            } else {
+                constexpr bool ADD = (MASK == MASK_ADD16 || MASK == MASK_ADD32);
+                // per-element mask; RAW: on unscaled scores (the scale is positive,
+                // so a masked -inf stays -inf once scaled); additive masks add to
+                // scaled scores
+                auto mask_scores = [&](auto raw_tag) __attribute__((always_inline)) {
+                    constexpr bool RAW = decltype(raw_tag)::value;
+                    float mtile = NEG_INF;
+    #pragma unroll
+                    for (int kb = 0; kb < C::NKB; ++kb) {
+    #pragma unroll
+                        for (int a4 = 0; a4 < 4; ++a4) {
+    #pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int j = kt + kb * 32 + 8 * a4 + 4 * hh + r;
+                                float x = sacc[kb][4 * a4 + r];
+                                if constexpr (!RAW) x *= c_scale;
+                                bool ok = true;
+                                if constexpr (TAIL) ok = j < kend;
+                                if constexpr (ADD)
+                                    x = __builtin_fmaf(mask_value<MASK>(mr[kb][a4], r, p.mask_dtype), kLog2e, x);
+                                if constexpr (MASK == MASK_CAUSAL) ok = ok && (j <= qi + off);
+                                if constexpr (MASK == MASK_SLIDE) ok = ok && in_window(j, qi + off, p.window);
+                                if constexpr (MASK == MASK_BOOL) ok = ok && ((mr[kb][a4] >> (8 * r)) & 0xffu) != 0u;
+                                x = ok ? x : NEG_INF;
+                                sacc[kb][4 * a4 + r] = x;
+                                mtile = fmaxf(mtile, x);
+                            }
                         }
                     }
+                    return mtile;
+                };
+                const float mt = mask_scores(PfTag<!ADD>{});
+                if (it + 1 < ntiles) load_mask(kt + BN);
+                if constexpr (ADD) softmax_pv(stage, sacc, mt, 1.f);
+                else softmax_pv(stage, sacc, mt * c_scale, c_scale);
+            }
+        };
+
+        // masked tiles left of the plain range (window edge), plain tiles, masked
+        // tiles right of it (diagonal, ragged end, or every tile of a mask tensor)
+        constexpr bool TAIL_CHECK = !CAUSAL_END;
+        int it = t0;
+        if (it < ntiles) issue_tile(it * BN, it & 1);
+        if constexpr (!HAS_MT) {
+            for (; it < tp0; ++it) tile(it, PfTag<true>{}, PfTag<false>{});
+            for (; it < tp1; ++it) tile(it, PfTag<false>{}, PfTag<false>{});
+        }
+        if (it < ntiles) load_mask(it * BN);
+        if constexpr (TAIL_CHECK) {
+            for (; it < ntiles - 1; ++it) tile(it, PfTag<true>{}, PfTag<false>{});
+            if (it < ntiles) tile(it, PfTag<true>{}, PfTag<true>{});
+        } else {
+            for (; it < ntiles; ++it) tile(it, PfTag<true>{}, PfTag<false>{});
+        }
+
+        // ---- epilogue ----
+        float lsum_row;
+        if constexpr (C::ONES) {
+            constexpr int rr = D % 32;
+            constexpr int RL = 4 * (rr / 8) + (rr % 4), HL = (rr % 8) / 4, DBL = D / 32;
+            const float x = oacc[DBL][RL];
+            const float y = xor32(x);
+            lsum_row = (hh == HL) ? x : y;
+        } else {
+            lsum_row = sum_x32(l_run);
+        }
+        if (rv) {
+            const float inv = lsum_row > 0.f ? 1.f / lsum_row : 0.f;
+            char* orow = reinterpret_cast<char*>(p.o) +
+                         ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2]) * 2;
+    #pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+    #pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int d0 = 32 * db + 8 * a4 + 4 * hh;
+                    if (d0 < D) {
+                        f32x4_t x = {oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv, oacc[db][4 * a4 + 2] * inv,
+                                     oacc[db][4 * a4 + 3] * inv};
+                        TR::store4(orow + d0 * 2, x);
+                    }
                 }
-                return mtile;
-            };
-            const float mt = mask_scores(PfTag<!ADD>{});
-            if (it + 1 < ntiles) load_mask(kt + BN);
-            if constexpr (ADD) softmax_pv(stage, sacc, mt, 1.f);
-            else softmax_pv(stage, sacc, mt * c_scale, c_scale);
         }
     };
-
-    // masked tiles left of the plain range (window edge), plain tiles, masked
-    // tiles right of it (diagonal, ragged end, or every tile of a mask tensor)
-    constexpr bool TAIL_CHECK = !CAUSAL_END;
-    int it = t0;
-    if (it < ntiles) issue_tile(it * BN, it & 1);
-    if constexpr (!HAS_MT) {
-        for (; it < tp0; ++it) tile(it, PfTag<true>{}, PfTag<false>{});
-        for (; it < tp1; ++it) tile(it, PfTag<false>{}, PfTag<false>{});
-    }
-    if (it < ntiles) load_mask(it * BN);
-    if constexpr (TAIL_CHECK) {
-        for (; it < ntiles - 1; ++it) tile(it, PfTag<true>{}, PfTag<false>{});
-        if (it < ntiles) tile(it, PfTag<true>{}, PfTag<true>{});
+    if constexpr (PAIRS) {
+        run(nqt - 1 - tt);
+        if (tt != nqt - 1 - tt) {
+            __syncthreads();  // every wave is done with the first row tile's LDS stages
+            run(tt);
+        }
     } else {
-        for (; it < ntiles; ++it) tile(it, PfTag<true>{}, PfTag<false>{});
-    }
-
-    // ---- epilogue ----
-    float lsum_row;
-    if constexpr (C::ONES) {
-        constexpr int rr = D % 32;
-        constexpr int RL = 4 * (rr / 8) + (rr % 4), HL = (rr % 8) / 4, DBL = D / 32;
-        const float x = oacc[DBL][RL];
-        const float y = xor32(x);
-        lsum_row = (hh == HL) ? x : y;
-    } else {
-        lsum_row = sum_x32(l_run);
-    }
-    if (rv) {
-        const float inv = lsum_row > 0.f ? 1.f / lsum_row : 0.f;
-        char* orow = reinterpret_cast<char*>(p.o) +
-                     ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2]) * 2;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int d0 = 32 * db + 8 * a4 + 4 * hh;
-                if (d0 < D) {
-                    f32x4_t x = {oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv, oacc[db][4 * a4 + 2] * inv,
-                                 oacc[db][4 * a4 + 3] * inv};
-                    TR::store4(orow + d0 * 2, x);
-                }
-            }
+        run(CAUSAL_END ? nqt - 1 - tt : tt);
     }
 }
 

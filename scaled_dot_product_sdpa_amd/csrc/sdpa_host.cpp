@@ -510,7 +510,9 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
             }
         const int bm = t.cols / hg;
         // one-dimensional grid: 8 XCDs x ceil(items / 8), items = (batch, head group, query tile)
-        const long items = (long)((q_len + bm - 1) / bm) * (n_q_heads / hg) * batch;
+        long qtiles = (q_len + bm - 1) / bm;
+        if (t.causal_pairs && mk == sdpa_dev::MASK_CAUSAL) qtiles = (qtiles + 1) / 2;  // two row tiles per item
+        const long items = qtiles * (n_q_heads / hg) * batch;
         if (items > (1L << 30)) return reject(SDPA_EUNSUPPORTED);
         dim3 grid((unsigned)(8 * ((items + 7) / 8)), 1, 1);
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
