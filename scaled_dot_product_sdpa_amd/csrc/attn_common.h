@@ -63,6 +63,7 @@ struct Params {
     int col_groups;   // decode: column groups per kv head
     int kbase;        // decode: first key of split 0 (keys before it are masked for every row)
     int window;       // MASK_SLIDE: keys per query (>= 1)
+    int pairs;        // prefill, causal: a workgroup takes row tiles t and last - t
     // rotary embedding of Q (0 = none): columns [0, rope_dim) of query row i
     // turn by the table angles of position rope_pos0 + i ([n_pos][rope_dim / 2] fp32)
     int rope_dim;

@@ -82,9 +82,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     const int col = lane & 31, hh = lane >> 5;
 
     // ---- work item (XCD-aware, longest causal tiles first) ----
-    constexpr bool PAIRS = C::PAIRS && MASK == MASK_CAUSAL;
+    const bool pairs = C::PAIRS && MASK == MASK_CAUSAL && p.pairs;  // the host's choice, uniform
     const int nqt = (p.Lq + BM - 1) / BM;
-    const int nit = PAIRS ? (nqt + 1) / 2 : nqt;  // row-tile items per head
+    const int nit = pairs ? (nqt + 1) / 2 : nqt;  // row-tile items per head
     const int total = nit * p.Hq * p.B;
     const int per = (total + 7) / 8;
     const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
@@ -105,9 +105,10 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         b = bh / p.Hq;
     }
     constexpr bool CAUSAL_END = (MASK == MASK_CAUSAL || MASK == MASK_SLIDE);
-    // the row tiles of one workgroup: one, or with PAIRS (causal) two whose
+    // the row tiles of one workgroup: one, or with pairs (causal) two whose
     // key ranges add up to the same length for every workgroup (t and nqt - 1 - t),
-    // so no single long row tile outlasts the rest of the grid
+    // so no single long row tile outlasts the rest of the grid (the host pairs
+    // only grids that still give every CU a workgroup)
     auto run = [&](const int t) __attribute__((always_inline)) {
         const int g = qh / p.n_rep;
         const int i0 = t * BM;
@@ -449,14 +450,10 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
                 }
         }
     };
-    if constexpr (PAIRS) {
-        run(nqt - 1 - tt);
-        if (tt != nqt - 1 - tt) {
-            __syncthreads();  // every wave is done with the first row tile's LDS stages
-            run(tt);
-        }
-    } else {
-        run(CAUSAL_END ? nqt - 1 - tt : tt);
+    run(CAUSAL_END ? nqt - 1 - tt : tt);
+    if (pairs && tt != nqt - 1 - tt) {
+        __syncthreads();  // every wave is done with the first row tile's LDS stages
+        run(tt);
     }
 }
 

@@ -31,7 +31,7 @@ using sdpa_host::launch_fn;
 namespace {
 
 constexpr int kVectorMaxQLen = 8;     // qL <= 8 -> vector kernel
-constexpr int kDeviceCUs = 256;       // MI355X compute units (split heuristic only)
+constexpr int kDeviceCUs = 256;       // MI355X compute units (grid heuristics only)
 constexpr int kMaxGridYZ = 65535;
 
 std::atomic<uint64_t> g_counters[4];  // calls, full, vector, rejected
@@ -199,6 +199,31 @@ const char* mask_name(sdpa_mask_kind mk) {
     return "?";
 }
 
+// Prefill grid: work items of (batch, head group, row tile).  A causal grid
+// pairs row tiles t and last - t in one workgroup (the same key count for
+// every workgroup, so no long row tile outlasts the rest) when the kernel
+// supports it and the halved grid still covers every CU.
+struct FullGrid {
+    long items;
+    int pairs;
+};
+FullGrid full_grid(const sdpa_host::TileInfo& t, bool causal, int batch, int q_len, int n_q_heads, int n_kv_heads) {
+    // heads of one group that share a workgroup: the largest power of two up
+    // to t.heads dividing the group size (the kernel derives the same number)
+    const int rep = n_q_heads / n_kv_heads;
+    int hg = 1;
+    for (int c = t.heads; c > 1; c >>= 1)
+        if (rep % c == 0) {
+            hg = c;
+            break;
+        }
+    const int bm = t.cols / hg;
+    const long qtiles = (q_len + bm - 1) / bm;
+    const long groups = (long)(n_q_heads / hg) * batch;
+    if (t.causal_pairs && causal && (qtiles + 1) / 2 * groups >= kDeviceCUs) return FullGrid{(qtiles + 1) / 2 * groups, 1};
+    return FullGrid{qtiles * groups, 0};
+}
+
 std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int d, int dv, sdpa_dtype dt,
                          sdpa_mask_kind mk, int st, sdpa_kernel k, int reason) {
     char buf[256];
@@ -215,10 +240,11 @@ std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int 
     const KernelSet* ks = kernel_set(dt, d, dv);
     if (k == SDPA_KERNEL_FULL) {
         const auto& t = ks->full_cfg;
+        const FullGrid fg = full_grid(t, mk == SDPA_MASK_CAUSAL, batch, q_len, hq, hkv);
         std::snprintf(buf, sizeof buf,
-                      "full %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d tile=%dx%d waves=%dx%d lds=%d",
+                      "full %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d tile=%dx%d waves=%dx%d lds=%d workgroups=%ld%s",
                       dtype_name(dt), dn, mask_name(mk), batch, q_len, kv_len, hq, hkv, t.cols, t.bn, t.wm, t.wd,
-                      t.lds);
+                      t.lds, fg.items, fg.pairs ? " causal-pairs" : "");
     } else {
         const auto& t = ks->dec_cfg;
         DecodePlan p = decode_plan(batch, q_len, kv_len, hq, hkv, t);
@@ -499,20 +525,9 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
 
     if (kern == SDPA_KERNEL_FULL) {
         const auto& t = ks->full_cfg;
-        // heads of one group that share a workgroup: the largest power of two up
-        // to t.heads dividing the group size (the kernel derives the same number)
-        const int rep = n_q_heads / n_kv_heads;
-        int hg = 1;
-        for (int c = t.heads; c > 1; c >>= 1)
-            if (rep % c == 0) {
-                hg = c;
-                break;
-            }
-        const int bm = t.cols / hg;
-        // one-dimensional grid: 8 XCDs x ceil(items / 8), items = (batch, head group, query tile)
-        long qtiles = (q_len + bm - 1) / bm;
-        if (t.causal_pairs && mk == sdpa_dev::MASK_CAUSAL) qtiles = (qtiles + 1) / 2;  // two row tiles per item
-        const long items = qtiles * (n_q_heads / hg) * batch;
+        const FullGrid fg = full_grid(t, mk == sdpa_dev::MASK_CAUSAL, batch, q_len, n_q_heads, n_kv_heads);
+        p.pairs = fg.pairs;
+        const long items = fg.items;
         if (items > (1L << 30)) return reject(SDPA_EUNSUPPORTED);
         dim3 grid((unsigned)(8 * ((items + 7) / 8)), 1, 1);
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,

@@ -139,6 +139,37 @@ def test_prefill_d512_reduced_seq_all_rows(gpu_lib):
 
 
 # --------------------------------------------------------------------------
+# Causal grids large enough for a workgroup to take two row tiles (t and
+# last - t): the route reports the pairing; every row (or, for the wide
+# heads, rows at the start and end of every row tile) against the oracle;
+# odd row-tile counts (the middle tile alone) and Lq < Lk.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("D,B,Hq,Hkv,Lq,Lk", [(64, 4, 16, 16, 1100, 1100), (72, 4, 16, 16, 1024, 1124),
+                                             (128, 4, 16, 8, 1100, 1100), (96, 2, 32, 4, 1152, 1300)])
+def test_causal_pairs_all_rows(gpu_lib, D, B, Hq, Hkv, Lq, Lk):
+    route = gpu_lib.describe_route(B, Lq, Lk, Hq, Hkv, D, torch.bfloat16, "causal")
+    assert "causal-pairs" in route, route
+    c = si.make_case(B, Hq, Hkv, Lq, Lk, D, dtype="bf16", layout="bhld", mask_kind="causal", seed=D + Lq)
+    assert_parity(run_gpu(c), oracle_out(c), "bf16", f"causal pairs D={D} B={B} Hq={Hq} Lq={Lq} Lk={Lk}")
+
+
+@pytest.mark.parametrize("D,B,Hq,Hkv,Lq,Lk,tile", [(256, 8, 16, 16, 1100, 1100, 256), (512, 4, 32, 4, 560, 600, 32)])
+def test_causal_pairs_wide_heads(gpu_lib, D, B, Hq, Hkv, Lq, Lk, tile):
+    route = gpu_lib.describe_route(B, Lq, Lk, Hq, Hkv, D, torch.bfloat16, "causal")
+    assert "causal-pairs" in route, route
+    c = si.make_case(B, Hq, Hkv, Lq, Lk, D, dtype="bf16", layout="bhld", mask_kind="causal", seed=D + Lq)
+    rows = sorted({r for t0 in range(0, Lq, tile) for r in (t0, t0 + 1, min(t0 + tile, Lq) - 1)})
+    out = run_gpu(c)
+    assert_parity(out[:, :, rows], oracle_out(c, q_rows=rows), "bf16", f"causal pairs D={D} Lq={Lq} Lk={Lk}")
+
+
+def test_causal_small_grid_is_not_paired(gpu_lib):
+    # 16 heads x 4096 rows at D = 256: 16 row tiles per head; halving them would idle half the CUs
+    assert "causal-pairs" not in gpu_lib.describe_route(1, 4096, 4096, 16, 16, 256, torch.bfloat16, "causal")
+    assert "causal-pairs" in gpu_lib.describe_route(1, 4096, 4096, 32, 32, 256, torch.bfloat16, "causal")
+
+
+# --------------------------------------------------------------------------
 # Sliding-window (local causal) attention: windows from one key to more than
 # the whole sequence, tiles that start left of, straddle and sit inside the
 # window, Lq < Lk (a key-value cache in front of the queries), GQA.
