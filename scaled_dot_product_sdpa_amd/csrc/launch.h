@@ -31,6 +31,11 @@ struct KernelSet {
     launch_fn combine;
     TileInfo full_cfg;
     TileInfo dec_cfg;
+    // causal prefill with fewer rows per workgroup, for grids too small to pair
+    // with full_cfg's workgroups (null where not built)
+    launch_fn full_small[sdpa_dev::MASK_VARIANTS];
+    launch_fn full_small_rope[sdpa_dev::MASK_VARIANTS];
+    TileInfo full_small_cfg;
 };
 
 // Returns hipErrorInvalidConfiguration when the compiled kernel cannot run

@@ -224,6 +224,24 @@ FullGrid full_grid(const sdpa_host::TileInfo& t, bool causal, int batch, int q_l
     return FullGrid{qtiles * groups, 0};
 }
 
+// The prefill kernel, its tile shape and grid: the default set, or, for a
+// causal grid that cannot pair, the variant with fewer rows per workgroup when
+// that one can pair or the default grid leaves CUs without a workgroup.
+struct FullPlan {
+    const sdpa_host::TileInfo* cfg;
+    FullGrid grid;
+    bool small;
+};
+FullPlan full_plan(const KernelSet* ks, int variant, int batch, int q_len, int n_q_heads, int n_kv_heads) {
+    const bool causal = variant == sdpa_dev::MASK_CAUSAL;
+    FullPlan fp{&ks->full_cfg, full_grid(ks->full_cfg, causal, batch, q_len, n_q_heads, n_kv_heads), false};
+    if (causal && !fp.grid.pairs && ks->full_small[variant]) {
+        const FullGrid gs = full_grid(ks->full_small_cfg, causal, batch, q_len, n_q_heads, n_kv_heads);
+        if (gs.pairs || fp.grid.items < kDeviceCUs) fp = FullPlan{&ks->full_small_cfg, gs, true};
+    }
+    return fp;
+}
+
 std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int d, int dv, sdpa_dtype dt,
                          sdpa_mask_kind mk, int st, sdpa_kernel k, int reason) {
     char buf[256];
@@ -239,8 +257,10 @@ std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int 
     }
     const KernelSet* ks = kernel_set(dt, d, dv);
     if (k == SDPA_KERNEL_FULL) {
-        const auto& t = ks->full_cfg;
-        const FullGrid fg = full_grid(t, mk == SDPA_MASK_CAUSAL, batch, q_len, hq, hkv);
+        const int variant = mk == SDPA_MASK_CAUSAL ? sdpa_dev::MASK_CAUSAL : sdpa_dev::MASK_NONE;
+        const FullPlan fp = full_plan(ks, variant, batch, q_len, hq, hkv);
+        const auto& t = *fp.cfg;
+        const FullGrid fg = fp.grid;
         std::snprintf(buf, sizeof buf,
                       "full %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d tile=%dx%d waves=%dx%d lds=%d workgroups=%ld%s",
                       dtype_name(dt), dn, mask_name(mk), batch, q_len, kv_len, hq, hkv, t.cols, t.bn, t.wm, t.wd,
@@ -524,15 +544,15 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     };
 
     if (kern == SDPA_KERNEL_FULL) {
-        const auto& t = ks->full_cfg;
-        const FullGrid fg = full_grid(t, mk == sdpa_dev::MASK_CAUSAL, batch, q_len, n_q_heads, n_kv_heads);
-        p.pairs = fg.pairs;
-        const long items = fg.items;
+        const FullPlan fp = full_plan(ks, mk, batch, q_len, n_q_heads, n_kv_heads);
+        p.pairs = fp.grid.pairs;
+        const long items = fp.grid.items;
         if (items > (1L << 30)) return reject(SDPA_EUNSUPPORTED);
         dim3 grid((unsigned)(8 * ((items + 7) / 8)), 1, 1);
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
                                     mask_kind, st, kern, reason));
-        const launch_fn f = p.rope_dim > 0 ? ks->full_rope[mk] : ks->full[mk];
+        const launch_fn f = fp.small ? (p.rope_dim > 0 ? ks->full_small_rope[mk] : ks->full_small[mk])
+                                     : (p.rope_dim > 0 ? ks->full_rope[mk] : ks->full[mk]);
         if (!f) return reject(SDPA_EUNSUPPORTED);
         mark(0);
         st = hip_status(f(p, grid, s));

@@ -172,3 +172,18 @@ def test_rope_arguments_are_checked_before_touching_the_gpu(lib):
     assert rope(tab, pos0=20) == -1                                   # positions past the table
     assert rope(tab, y=4096 + 64) == -1                               # partial overlap of x and y
     assert rope(tab, dt=3) == -2                                      # u8 is a mask type only
+
+
+# causal prefill grids: the route names the tile shape and whether row tiles pair
+def test_causal_small_grids_route(lib):
+    import torch
+    import scaled_dot_product_sdpa_amd as sdpa
+    route = lambda h, d: sdpa.describe_route(1, 4096, 4096, h, h, d, torch.bfloat16, "causal")
+    # 32 heads at D = 256: 256-row workgroups, paired
+    assert "waves=8x1" in route(32, 256) and "causal-pairs" in route(32, 256)
+    # 16 heads: 256-row workgroups could not pair without idling CUs; 128-row ones pair
+    assert "waves=4x1" in route(16, 256) and "causal-pairs" in route(16, 256)
+    # 8 heads: 128-row workgroups fill the CUs unpaired
+    assert "waves=4x1" in route(8, 256) and "causal-pairs" not in route(8, 256)
+    # D = 512 has no smaller variant: 8 heads stay unpaired on 256 workgroups
+    assert "waves=8x2" in route(8, 512) and "causal-pairs" not in route(8, 512)

@@ -163,10 +163,15 @@ def test_causal_pairs_wide_heads(gpu_lib, D, B, Hq, Hkv, Lq, Lk, tile):
     assert_parity(out[:, :, rows], oracle_out(c, q_rows=rows), "bf16", f"causal pairs D={D} Lq={Lq} Lk={Lk}")
 
 
-def test_causal_small_grid_is_not_paired(gpu_lib):
-    # 16 heads x 4096 rows at D = 256: 16 row tiles per head; halving them would idle half the CUs
-    assert "causal-pairs" not in gpu_lib.describe_route(1, 4096, 4096, 16, 16, 256, torch.bfloat16, "causal")
-    assert "causal-pairs" in gpu_lib.describe_route(1, 4096, 4096, 32, 32, 256, torch.bfloat16, "causal")
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("H,L", [(16, 4096), (8, 2000)])
+def test_causal_small_grid_variant(gpu_lib, dtype, H, L):
+    route = gpu_lib.describe_route(1, L, L, H, H, 256, si.DTYPES[dtype], "causal")
+    assert "waves=4x1" in route, route
+    c = si.make_case(1, H, H, L, L, 256, dtype=dtype, layout="blhd", mask_kind="causal", seed=H + L)
+    rows = sorted({r for t0 in range(0, L, 128) for r in (t0, min(t0 + 127, L - 1))} | {L // 2 + 3})
+    out = run_gpu(c)
+    assert_parity(out[:, :, rows], oracle_out(c, q_rows=rows), dtype, f"causal small grid D=256 H={H} L={L} {dtype}")
 
 
 # --------------------------------------------------------------------------
