@@ -274,6 +274,9 @@ __device__ __forceinline__ typename MaskRaw<MASK>::type load_mask_group_rs(__amd
 
 // Any other layout: the group's 4 elements one by one (element offsets
 // row_off + (key0 + k) * key_stride), through the same kind of resource.
+// The prefill kernels take this path in a separate instantiation (SMASK):
+// the compiler keeps a per-lane offset for every group of a tile live across
+// the key loop, registers the vector path must not pay for.
 template <int MASK>
 __device__ __forceinline__ typename MaskRaw<MASK>::type load_mask_group_rs_strided(__amdgpu_buffer_rsrc_t r,
                                                                                     uint32_t row_off, int key0,

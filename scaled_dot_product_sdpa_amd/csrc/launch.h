@@ -36,6 +36,11 @@ struct KernelSet {
     launch_fn full_small[sdpa_dev::MASK_VARIANTS];
     launch_fn full_small_rope[sdpa_dev::MASK_VARIANTS];
     TileInfo full_small_cfg;
+    // prefill with a mask tensor whose keys are not aligned 4-element runs
+    // (Params::mask_vec == 0), same tiles as full_cfg (null where full[]
+    // handles both layouts)
+    launch_fn full_strided[sdpa_dev::MASK_VARIANTS];
+    launch_fn full_strided_rope[sdpa_dev::MASK_VARIANTS];
 };
 
 // Returns hipErrorInvalidConfiguration when the compiled kernel cannot run

@@ -70,7 +70,9 @@ struct PfCfg {
 
 template <bool B> struct PfTag { static constexpr bool value = B; };
 
-template <class TR, class C, int MASK, bool ROPE = false>
+// SMASK: the mask tensor's keys are not 4-element aligned runs (mask_vec == 0);
+// its elements are loaded one by one.
+template <class TR, class C, int MASK, bool ROPE = false, bool SMASK = false>
 __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) {
     constexpr int D = C::D, BN = C::BN, BM = C::BM;
     constexpr float NEG_INF = -__builtin_inff();
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         typename MaskRaw<MASK>::type mr[HAS_MT ? C::NKB : 1][4];
         auto load_mask = [&](int kt) {
             if constexpr (HAS_MT) {
-                if (p.mask_vec) {
+                if constexpr (!SMASK) {
     #pragma unroll
                     for (int kb = 0; kb < C::NKB; ++kb)
     #pragma unroll

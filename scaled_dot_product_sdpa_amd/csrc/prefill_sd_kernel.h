@@ -62,7 +62,9 @@ struct SdCfg {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <class TR, class C, int MASK, bool ROPE = false>
+// SMASK: the mask tensor's keys are not 4-element aligned runs (mask_vec == 0);
+// its elements are loaded one by one.
+template <class TR, class C, int MASK, bool ROPE = false, bool SMASK = false>
 __global__ __launch_bounds__(C::NT, C::WPE) void prefill_sd_kernel(const Params p) {
     constexpr int D = C::D, BN = C::BN, NW = C::NW, NS = C::NS, DH = C::DH;
     constexpr float NEG_INF = -__builtin_inff();
@@ -208,14 +210,21 @@ __global__ __launch_bounds__(C::NT, C::WPE) void prefill_sd_kernel(const Params 
         typename MaskRaw<MASK>::type mr[HAS_MT ? C::NKB : 1][4];
         auto load_mask = [&](int kt) __attribute__((always_inline)) {
             if constexpr (HAS_MT) {
+                if constexpr (!SMASK) {
     #pragma unroll
-                for (int kb = 0; kb < C::NKB; ++kb)
+                    for (int kb = 0; kb < C::NKB; ++kb)
     #pragma unroll
-                    for (int a4 = 0; a4 < 4; ++a4) {
-                        const int key0 = kt + kb * 32 + 8 * a4 + 4 * hh;
-                        mr[kb][a4] = p.mask_vec ? load_mask_group_rs<MASK>(mrs, (mlane + (uint32_t)key0) * MES)
-                                                : load_mask_group_rs_strided<MASK>(mrs, mlane, key0, (uint32_t)p.ms[3]);
-                    }
+                        for (int a4 = 0; a4 < 4; ++a4)
+                            mr[kb][a4] = load_mask_group_rs<MASK>(
+                                mrs, (mlane + (uint32_t)(kt + kb * 32 + 8 * a4 + 4 * hh)) * MES);
+                } else {
+    #pragma unroll
+                    for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                        for (int a4 = 0; a4 < 4; ++a4)
+                            mr[kb][a4] = load_mask_group_rs_strided<MASK>(mrs, mlane, kt + kb * 32 + 8 * a4 + 4 * hh,
+                                                                          (uint32_t)p.ms[3]);
+                }
             }
         };
 

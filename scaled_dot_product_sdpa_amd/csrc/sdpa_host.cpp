@@ -551,8 +551,10 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         dim3 grid((unsigned)(8 * ((items + 7) / 8)), 1, 1);
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
                                     mask_kind, st, kern, reason));
-        const launch_fn f = fp.small ? (p.rope_dim > 0 ? ks->full_small_rope[mk] : ks->full_small[mk])
-                                     : (p.rope_dim > 0 ? ks->full_rope[mk] : ks->full[mk]);
+        const bool strided = !p.mask_vec && ks->full_strided[mk];
+        const launch_fn f = fp.small     ? (p.rope_dim > 0 ? ks->full_small_rope[mk] : ks->full_small[mk])
+                            : strided    ? (p.rope_dim > 0 ? ks->full_strided_rope[mk] : ks->full_strided[mk])
+                                         : (p.rope_dim > 0 ? ks->full_rope[mk] : ks->full[mk]);
         if (!f) return reject(SDPA_EUNSUPPORTED);
         mark(0);
         st = hip_status(f(p, grid, s));

@@ -261,14 +261,19 @@ def test_large_scores(gpu_lib, D, lq, dtype, mask_kind):
 # --------------------------------------------------------------------------
 # Mask tensors in layouts without the vector fast path: keys strided (a
 # transposed view), rows not a multiple of 4 elements apart, misaligned base.
+# The 16-bit prefill kernels run these in separate instantiations that load
+# mask elements one by one; with the same values in a plain contiguous tensor
+# the output must be the same bit for bit.
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("layout", ["key_strided", "odd_rows", "offset_base"])
-@pytest.mark.parametrize("mask_kind", ["boolean", "additive"])
-@pytest.mark.parametrize("D,lq", [(72, 150), (128, 70), (256, 90), (64, 5)])
+@pytest.mark.parametrize("mask_kind", ["boolean", "additive", "additive_f32"])
+@pytest.mark.parametrize("D,lq", [(72, 150), (128, 70), (256, 90), (512, 40), (64, 5)])
 def test_mask_layouts_without_vector_loads(gpu_lib, D, lq, mask_kind, layout):
     lk = 131 if layout == "odd_rows" else 132
+    mdt = "f32" if mask_kind == "additive_f32" else None
+    mask_kind = "additive" if mask_kind == "additive_f32" else mask_kind
     c = si.make_case(1, 4, 2, lq, lk, D, dtype="bf16", layout="bhld", mask_kind=mask_kind, seed=D + lq,
-                     mask_shape="qk", mask_p=0.3)
+                     mask_shape="qk", mask_p=0.3, mask_dtype=mdt)
     q, k, v, _ = to_device(c)
     m = c.mask
     if layout == "key_strided":
@@ -281,8 +286,11 @@ def test_mask_layouts_without_vector_loads(gpu_lib, D, lq, mask_kind, layout):
         dm = m.cuda()
     assert torch.equal(dm.cpu(), m)
     out = gpu_lib.forward(q, k, v, scale=c.scale, mask=dm, mask_kind=mask_kind)
+    plain = gpu_lib.forward(q, k, v, scale=c.scale, mask=m.contiguous().cuda(), mask_kind=mask_kind)
     torch.cuda.synchronize()
     assert_parity(out, oracle_out(c), "bf16", f"mask layout {layout} {mask_kind} D={D} Lq={lq}")
+    if layout != "odd_rows":  # (with odd_rows the contiguous tensor itself has no vector layout)
+        assert torch.equal(out, plain), f"mask layout {layout} {mask_kind} D={D}: differs from the contiguous mask"
 
 
 # --------------------------------------------------------------------------
