@@ -40,6 +40,9 @@ CASES = [
                                       layout="blhd"), "full", "causal-pairs"),
     ("prefill-d128-boolean", dict(B=1, Hq=4, Hkv=2, Lq=300, Lk=333, D=128, mask_kind="boolean",
                                   mask_shape="qk"), "full", ""),
+    # (a launch with dynamic LDS padding: mask tensors below D = 128)
+    ("prefill-d72-additive", dict(B=1, Hq=4, Hkv=2, Lq=300, Lk=332, D=72, mask_kind="additive",
+                                  mask_shape="qk"), "full", ""),
     ("prefill-d256-sliding", dict(B=1, Hq=4, Hkv=2, Lq=500, Lk=500, D=256, mask_kind="sliding", window=100),
      "full", ""),
     ("prefill-d512-causal", dict(B=1, Hq=8, Hkv=1, Lq=400, Lk=400, D=512, mask_kind="causal"), "full", ""),

@@ -126,6 +126,23 @@ def test_fused_rope_qk192_v128(gpu_lib, dtype, R):
     assert_parity(out, ref, dtype, f"fused rope qk192/v128 R={R} {dtype}")
 
 
+@pytest.mark.parametrize("mask_kind", ["boolean", "additive"])
+@pytest.mark.parametrize("D,R", [(72, 64), (128, 128), (256, 64), (512, 128)])
+def test_fused_rope_with_strided_mask(gpu_lib, D, R, mask_kind):
+    """A mask whose keys are strided goes through the element-wise mask
+    instantiations with the rotary prologue: same bits as the contiguous mask."""
+    import scaled_dot_product_sdpa_amd as sdpa
+    c, k_rot, rope, pos0, ref = fused_case(1, 4, 2, 150, 164, D, R, "bf16", mask_kind, seed=D + 7)
+    plain = run_fused(c, k_rot, rope, pos0)
+    dm = c.mask.transpose(-1, -2).contiguous().cuda().transpose(-1, -2)
+    assert torch.equal(dm.cpu(), c.mask)
+    out = sdpa.forward(c.q.cuda(), k_rot.cuda(), c.v.cuda(), scale=c.scale, mask=dm, mask_kind=mask_kind,
+                       rope=rope, q_pos0=pos0)
+    torch.cuda.synchronize()
+    assert_parity(out, ref, "bf16", f"fused rope strided {mask_kind} mask D={D} R={R}")
+    assert torch.equal(out, plain), f"fused rope D={D}: strided and contiguous masks differ"
+
+
 def test_fused_rope_explicit_positions_and_blhd(gpu_lib):
     # queries of a chunk in the middle of a long sequence: positions 3000.. read deep table rows
     c, k_rot, rope, pos0, ref = fused_case(2, 6, 3, 64, 90, 128, 128, "bf16", "none", seed=5, q_pos0=3000,
