@@ -8,22 +8,33 @@ seeded synthetic input already resident in HBM.  The headline workload is the
 bf16 grouped-query decode with head dim 256 (B=1, qL=1, Hq=32, Hkv=8,
 Lk=4096, additive [1,1,1,Lk] mask): value = K+V bytes per step / step time.
 Decode steps rotate over enough K/V replicas (> 2 x the 256 MB Infinity
-Cache) that every step reads cold HBM.  K steps are captured in one HIP
-graph and replayed (the host launch cost of the Python binding would
-otherwise dominate a ~10 us step); the eager per-step time is reported too.
+Cache) that every step reads cold HBM.  The K steps of a workload are
+captured in one HIP graph; after an untimed replay, one replay is timed with
+HIP events on the replaying stream, bracketed by synchronisations (the host
+launch cost of the Python binding would otherwise dominate a ~10 us step).
 
-roofline: the dominant kernel's algorithmic work per launch / its average
-duration, timed with HIP events the library records around each launch on
-the launch stream (sdpa_timing_start/stop); traffic from rocprofv3 counters
-(profiles/counters.json) when they were taken on the current kernel sources.
-cpu_baseline: the float64 oracle on the host, on a bounded sample.
+roofline (per workload): algorithmic work per step (decode: K+V bytes;
+prefill: 4 B Hq Lq Lk D flops, halved for causal) / the graph-timed step.
+Every workload listed here runs one kernel launch per step, so this is also
+that kernel's launch-to-launch duration, the figure rocprofv3's kernel trace
+gives for back-to-back launches (`--summarize-trace` derives it from a
+trace).  traffic: HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
+counters (profiles/counters.json) when they were taken on the current
+kernel sources.
+ceiling: one launch of the library's plain streaming read of the same number
+of bytes as the headline decode, timed the same way (cold replicas, graph).
+cpu_baseline: the float64 oracle on the host, one process per core, one
+(batch, head) per task, on a bounded sample of each workload.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -35,6 +46,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix
 COLD_BYTES = 600 << 20         # K/V replicas per decode run: > 2 x 256 MB Infinity Cache
+MAX_POOL = 16                  # host cores one GPU's share may use
 
 WORKLOADS = {
     "decode-d256-lk4096": dict(kind="decode", D=256, Lk=4096),
@@ -51,26 +63,19 @@ WORKLOADS = {
     "tiny-f32": dict(kind="tiny"),
 }
 PRIMARY = "decode-d256-lk4096"
-
-
-# kernel sources each workload's kernels are built from (counters taken on
-# other sources are stale)
-KERNEL_SOURCES = {
-    "decode": ["attn_common.h", "decode_kernel.h", "attn_kernel.h", "launch.h", "inst_template.hip.in"],
-    "prefill72": ["attn_common.h", "prefill_kernel.h", "launch.h", "inst_template.hip.in"],
-    "prefill512": ["attn_common.h", "prefill_sd_kernel.h", "launch.h", "inst_template.hip.in"],
-    "sliding": ["attn_common.h", "prefill_sd_kernel.h", "decode_kernel.h", "attn_kernel.h", "launch.h",
-                "inst_template.hip.in"],
-    "decode_dv": ["attn_common.h", "decode_kernel.h", "attn_kernel.h", "launch.h", "inst_pair_template.hip.in"],
-    "tiny": ["attn_common.h", "attn_kernel.h", "tile_configs.h", "launch.h", "inst_template.hip.in"],
-}
+PREFILL = ("prefill-d512-causal", "prefill-d72-none", "prefill-d72-causal", "prefill-d72-boolean")
+CPU_WORKLOADS = ("decode-d256-lk4096", "decode-d512-lk4096", "prefill-d72-none", "prefill-d72-boolean",
+                 "prefill-d72-causal", "prefill-d512-causal")
 
 
 def kernel_hash(name: str = PRIMARY) -> str:
-    """Hash of the sources of `name`'s kernels."""
+    """Hash of every source the library is built from (any change makes counters stale)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[WORKLOADS[name]["kind"]]:
-        h.update(open(os.path.join(ROOT, "scaled_dot_product_sdpa_amd", "csrc", f), "rb").read())
+    files = sorted(glob.glob(os.path.join(ROOT, "scaled_dot_product_sdpa_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "sdpa.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -121,30 +126,52 @@ def work(c) -> tuple[float, str]:
     return (f / 2 if c.mask_kind == "causal" else f), "flops"
 
 
-def to_device_replicas(c, n):
+def launches_per_step(route: str) -> int:
+    """Kernel launches one call makes: the split + combine decode route makes two."""
+    if route.startswith("vector ") and "splits=1 " not in route:
+        return 2
+    return 1
+
+
+def graph_time(step, steps: int) -> float:
+    """ms per step: `steps` calls captured in one graph, one untimed replay, one timed replay."""
     import torch
-    import sdpa_inputs as si
-    reps = [si.to_device(c) for _ in range(n)]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
     torch.cuda.synchronize()
-    return reps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
-def measure(name: str, steps: int, warmup: int) -> dict:
+def measure(name: str, steps: int, warmup: int, eager: bool = False) -> dict:
     import torch
     import scaled_dot_product_sdpa_amd as sdpa
+    import sdpa_inputs as si
 
     c = make_case(name)
     amount, unit = work(c)
     decode = unit == "bytes"
     kv_bytes = 2 * c.k.numel() * c.k.element_size()
     nrep = max(2, -(-COLD_BYTES // kv_bytes)) if decode else 1
-    reps = to_device_replicas(c, nrep)
+    reps = [si.to_device(c) for _ in range(nrep)]
+    torch.cuda.synchronize()
     q0 = reps[0][0]
     out = torch.empty(q0.shape[:3] + (c.v.shape[3],), dtype=q0.dtype, device="cuda")
     d = c.dims
     ws_bytes = sdpa.workspace_size(d["batch"], d["q_len"], d["kv_len"], d["n_q_heads"], d["n_kv_heads"],
                                    d["head_dim"], q0.dtype, v_head_dim=c.v.shape[3])
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 32768), dtype=torch.uint8, device="cuda")  # arrival words start at zero
 
     def step(i):
         q, k, v, m = reps[i % nrep]
@@ -154,108 +181,125 @@ def measure(name: str, steps: int, warmup: int) -> dict:
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-
-    # eager steps (host launch cost included)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / steps
-
-    # per-kernel times from events recorded by the library on the launch stream
-    with sdpa.kernel_timing(steps) as kt:
+    eager_ms = None
+    if eager:  # host launch cost included
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         for i in range(steps):
             step(i)
-    torch.cuda.synchronize()
-    k_ms = sorted(t[0] for t in kt.ms)
-    c_ms = [t[1] for t in kt.ms]
-    kernel_ms = sum(k_ms) / len(k_ms)
-    combine_ms = sum(c_ms) / len(c_ms)
-
-    # graph: K steps captured once, replayed (warm-up replay, then the timed one)
-    graph_ms = None
-    try:
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                for i in range(steps):
-                    step(i)
-        torch.cuda.current_stream().wait_stream(s)
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        g.replay()
         e1.record()
         torch.cuda.synchronize()
-        graph_ms = e0.elapsed_time(e1) / steps
-    except Exception as ex:  # graph capture unavailable: report eager only
-        print(f"[bench] graph capture failed: {ex}", file=sys.stderr)
-    ms = graph_ms if graph_ms is not None else eager_ms
+        eager_ms = e0.elapsed_time(e1) / steps
+    ms = graph_time(step, steps)
     route = sdpa.describe_route(d["batch"], d["q_len"], d["kv_len"], d["n_q_heads"], d["n_kv_heads"],
                                 d["head_dim"], q0.dtype, c.mask_kind, v_head_dim=c.v.shape[3])
-    res = dict(config=describe(name, c), route=route, ms_per_step=ms, eager_ms_per_step=eager_ms,
-               graph_ms_per_step=graph_ms, kernel_ms=kernel_ms, kernel_ms_p10=k_ms[len(k_ms) // 10],
-               kernel_ms_p90=k_ms[(9 * len(k_ms)) // 10], combine_ms=combine_ms, replicas=nrep,
-               work=amount, work_unit=unit)
     if decode:
-        res.update(value=amount / (ms * 1e-3) / 1e9, unit="GB/s",
-                   kernel_rate=amount / (kernel_ms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, bound="hbm", rate_unit="GB/s")
+        rate, runit, peak, bound = amount / (ms * 1e-3) / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"
     else:
-        peak = FP32_PEAK_TFLOPS if str(q0.dtype) == "torch.float32" else BF16_PEAK_TFLOPS
-        res.update(value=amount / (ms * 1e-3) / 1e12, unit="TFLOP/s",
-                   kernel_rate=amount / (kernel_ms * 1e-3) / 1e12, peak=peak, bound="mfma", rate_unit="TFLOP/s")
-    res["frac"] = res["kernel_rate"] / res["peak"]
+        peak = FP32_PEAK_TFLOPS if q0.dtype == torch.float32 else BF16_PEAK_TFLOPS
+        rate, runit, bound = amount / (ms * 1e-3) / 1e12, "TFLOP/s", "mfma"
+    nl = launches_per_step(route)
+    roof = {"bound": bound, "achieved": rate, "peak": peak, "unit": runit, "frac": rate / peak,
+            "traffic": load_traffic(name), "launches_per_step": nl, "launch_ms": ms / nl,
+            "work_per_launch": amount, "work_unit": unit}
+    res = dict(config=describe(name, c), route=route, value=rate, unit=runit, ms_per_step=ms,
+               eager_ms_per_step=eager_ms, replicas=nrep, roofline=roof)
     del reps
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(name: str, budget_s: float) -> dict:
-    """The float64 oracle, as it is, on the host; a bounded sample of the same workload."""
+def ceiling(nbytes: int, steps: int) -> dict:
+    """The library's plain streaming read of nbytes, cold, timed like a decode step."""
+    import torch
+    import scaled_dot_product_sdpa_amd as sdpa
+    nrep = max(2, -(-COLD_BYTES // nbytes))
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nrep)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for i in range(3):
+        sdpa.probe_stream_read(bufs[i % nrep], sink)
+    ms = graph_time(lambda i: sdpa.probe_stream_read(bufs[i % nrep], sink), steps)
+    rate = nbytes / (ms * 1e-3) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "ms_per_launch": ms, "value": rate, "unit": "GB/s", "frac": rate / HBM_PEAK_GBS,
+            "kernel": "stream_read_kernel (one 256-thread workgroup per CU, 8 x 16-byte loads in flight)"}
+
+
+# ---------------------------------------------------------------- CPU baseline
+def _oracle_task(args):
+    """One (batch, query head) of a workload through the float64 oracle, single-threaded BLAS."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
     import oracle
+    q, k, v, scale, kind, mask, rows = args
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oracle.sdpa(q, k, v, np.float32(scale), kind, mask, q_rows=rows)
+        return time.perf_counter() - t0
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(name: str, budget_s: float, pool, cores: int) -> dict:
+    """The float64 oracle, as it is, on a bounded sample of the workload: (batch, query
+    head) tasks spread over a process pool, rows sampled for long prefills."""
+    import numpy as np
     c = make_case(name)
     amount, unit = work(c)
+    d = c.dims
+    B, Hq, Hkv, Lq = d["batch"], d["n_q_heads"], d["n_kv_heads"], d["q_len"]
+    rep = Hq // Hkv
+    q, k, v = (t.double().numpy() for t in (c.q, c.k, c.v))
     mask = None
     if c.mask_kind == "sliding":
         mask = c.meta["window"]
     elif c.mask is not None:
         mask = c.mask.double().numpy() if c.mask_kind == "additive" else c.mask.numpy()
-    q, k, v = (t.double().numpy() for t in (c.q, c.k, c.v))
-    Lq = q.shape[2]
-    rows = None
-    frac = 1.0
-    if Lq > 64:  # prefill: a sample of query rows, scaled
+    rows, frac_rows = None, 1.0
+    if Lq > 64:  # prefill: evenly spaced query rows, work scaled by their share
         n = 64
         rows = np.linspace(0, Lq - 1, n).astype(np.int64)
-        frac = n / Lq
+        frac_rows = n / Lq
+        if c.mask_kind == "causal":  # a causal row's work grows with its index: scale by the keys kept
+            off = d["kv_len"] - Lq
+            frac_rows = float(sum(min(d["kv_len"], int(r) + off + 1) for r in rows)) / (Lq * (Lq + 1) / 2)
+    tasks = []
+    for b in range(B):
+        for h in range(Hq):
+            g = h // rep
+            m = mask
+            if isinstance(mask, np.ndarray):
+                m = mask[min(b, mask.shape[0] - 1):min(b, mask.shape[0] - 1) + 1,
+                         min(h, mask.shape[1] - 1):min(h, mask.shape[1] - 1) + 1]
+            tasks.append((q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], c.scale, c.mask_kind, m,
+                          rows))
+    per_call = amount * frac_rows  # one full pass over every (b, h), sampled rows
     t0 = time.perf_counter()
-    calls = 0
+    passes = 0
     while True:
-        oracle.sdpa(q, k, v, np.float32(c.scale), c.mask_kind, mask, q_rows=rows)
-        calls += 1
+        list(pool.map(_oracle_task, tasks))
+        passes += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = (time.perf_counter() - t0) / calls
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
-    # the oracle computes every (row, key) pair: scale the sampled rows' share of the work
-    per_call = amount * frac
+    dt = (time.perf_counter() - t0) / passes
     if unit == "bytes":
         val, u = per_call / dt / 1e9, "GB/s"
     else:
         val, u = per_call / dt / 1e12, "TFLOP/s"
-    sample = (f"{name}: full call ({calls} calls in {dt * calls:.1f}s)" if rows is None else
-              f"{name}: {len(rows)} of {Lq} query rows per call, work scaled by {frac:.4f} ({calls} calls)")
+    sample = (f"{name}: every (batch, head) of one call, {passes} passes in {dt * passes:.1f}s" if rows is None else
+              f"{name}: {len(rows)} of {Lq} query rows of every (batch, head), work scaled by "
+              f"{frac_rows:.4f}, {passes} passes in {dt * passes:.1f}s")
     return {"value": val, "unit": u, "cores": cores, "kind": "oracle", "sample": sample,
-            "seconds_per_call": dt}
+            "seconds_per_call": dt / frac_rows, "cpu_model": cpu_model(), "tasks": len(tasks)}
 
 
 def load_traffic(name: str):
@@ -272,6 +316,91 @@ def load_traffic(name: str):
     return ent.get("hbm_bytes_per_launch")
 
 
+# ------------------------------------------------------- rocprofv3 post-processing
+def _short(kernel: str) -> str:
+    s = kernel.split("(")[0].replace("sdpa_dev::", "").replace("void ", "")
+    return s
+
+
+def summarize_trace(trace_csv: str, command: str) -> str:
+    """Markdown summary of a rocprofv3 kernel trace: per kernel and grid, the average duration
+    over every launch and over back-to-back launches (a launch that starts when the previous
+    one ends: the graph-replayed steps, whose durations include the launch's fixed cost)."""
+    rows = list(csv.DictReader(open(trace_csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    stats = {}
+    prev_end = None
+    for r in rows:
+        s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1)) *
+               int(r.get("Grid_Size_Z", 1)) // max(1, int(r["Workgroup_Size_X"])))
+        ent = stats.setdefault(key, {"all": [], "b2b": []})
+        ent["all"].append((e - s) / 1000.0)
+        if prev_end is not None and s - prev_end <= 500:  # within 0.5 us of the previous launch's end
+            ent["b2b"].append((e - s) / 1000.0)
+        prev_end = e
+    out = [f"Command (repo root, one MI355X, `export TMPDIR=/tmp`):", "", "```", command, "```", "",
+           "| kernel | workgroups | launches | avg us (all) | back-to-back launches | avg us (back-to-back) |",
+           "|---|---|---|---|---|---|"]
+    for (k, wg), ent in sorted(stats.items(), key=lambda x: -sum(x[1]["all"])):
+        a, bb = ent["all"], ent["b2b"]
+        if k.startswith("__amd") or k.startswith("at::") or len(a) < 3:
+            continue
+        out.append(f"| `{k}` | {wg} | {len(a)} | {sum(a) / len(a):.2f} | {len(bb)} | "
+                   f"{(sum(bb) / len(bb)) if bb else float('nan'):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def ingest_counters(pmc_dir: str, calib_bytes: int):
+    """counters.json from rocprofv3 --pmc passes: <pmc_dir>/<counter>_<workload>/.../*counter_collection.csv,
+    with <counter>_copy holding a device-to-device copy of calib_bytes for the scale factor."""
+    def per_dispatch(pattern, counter, kernel_filter=None):
+        vals = {}
+        for f in glob.glob(os.path.join(pmc_dir, pattern, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r.get("Counter_Name") != counter:
+                    continue
+                kn = r["Kernel_Name"]
+                if kernel_filter and not kernel_filter(kn):
+                    continue
+                vals.setdefault((kn, r["Dispatch_Id"]), 0.0)
+                vals[(kn, r["Dispatch_Id"])] += float(r["Counter_Value"])
+        return vals
+    out = {"note": "HBM bytes per launch of each workload's kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, "
+                   "one rocprofv3 --pmc pass each) times the factor a device-to-device copy of known size gives "
+                   "for the same counter", "calibration": {}, "workloads": {}}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        v = per_dispatch(f"{counter}_copy", counter, lambda k: "copy" in k.lower())
+        big = max(v.values()) if v else 0.0
+        out["calibration"][counter] = {"copy_bytes": calib_bytes, "counter_kib_per_copy": big,
+                                       "factor": calib_bytes / (big * 1024.0) if big else None}
+    for d in sorted(glob.glob(os.path.join(pmc_dir, "FETCH_SIZE_*"))):
+        name = os.path.basename(d)[len("FETCH_SIZE_"):]
+        if name == "copy" or name not in WORKLOADS:
+            continue
+        ent = {"kernel_hash": kernel_hash(name)}
+        for counter, key in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
+            v = per_dispatch(f"{counter}_{name}", counter, lambda k: "sdpa_dev" in k)
+            if not v:
+                continue
+            kern = max(set(k for k, _ in v), key=lambda kk: sum(x for (k2, _), x in v.items() if k2 == kk))
+            xs = [x for (k, _), x in v.items() if k == kern]
+            f = out["calibration"][counter]["factor"] or 1.0
+            ent["kernel"] = _short(kern)
+            ent[f"{key}_kib_per_dispatch"] = sum(xs) / len(xs)
+            ent[f"hbm_{key}_bytes_per_launch"] = sum(xs) / len(xs) * 1024.0 * f
+            ent["dispatches"] = len(xs)
+        if "hbm_read_bytes_per_launch" in ent and "hbm_write_bytes_per_launch" in ent:
+            ent["hbm_bytes_per_launch"] = ent["hbm_read_bytes_per_launch"] + ent["hbm_write_bytes_per_launch"]
+            c = make_case(name)
+            ent["algorithmic_per_launch"], ent["algorithmic_unit"] = work(c)
+            qkv = sum(t.numel() * t.element_size() for t in (c.q, c.k, c.v))
+            ent["qkv_bytes"] = qkv
+            ent["o_bytes"] = c.q.shape[0] * c.q.shape[1] * c.q.shape[2] * c.v.shape[3] * c.q.element_size()
+        out["workloads"][name] = ent
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,12 +409,27 @@ def main():
     ap.add_argument("--workload", default=PRIMARY, choices=sorted(WORKLOADS))
     ap.add_argument("--no-secondary", action="store_true", help="skip the other configurations")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=3.0, help="oracle budget per workload")
+    ap.add_argument("--eager", action="store_true", help="also time eager (host-launched) steps")
     ap.add_argument("--profile-run", action="store_true",
                     help="only run --steps eager calls of --workload (for rocprofv3), print nothing else")
     ap.add_argument("--profile-copy", type=int, default=0, metavar="MIB",
                     help="only run --steps device-to-device copies of MIB MiB (calibrates rocprofv3 byte counters)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("CSV", "COMMAND"),
+                    help="print a markdown summary of a rocprofv3 kernel trace (no GPU needed)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("DIR", "COPY_MIB"),
+                    help="write profiles/counters.json from rocprofv3 --pmc output (no GPU needed)")
     a = ap.parse_args()
+
+    if a.summarize_trace:
+        print(summarize_trace(*a.summarize_trace))
+        return
+    if a.ingest_counters:
+        res = ingest_counters(a.ingest_counters[0], int(a.ingest_counters[1]) << 20)
+        with open(os.path.join(ROOT, "profiles", "counters.json"), "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res, indent=1))
+        return
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "one GPU only: a multi-GPU run (sharding by kv head) is not implemented",
@@ -315,7 +459,7 @@ def main():
         import sdpa_inputs as si
         q, k, v, m = si.to_device(c)
         d = c.dims
-        ws = torch.empty(max(256, sdpa.workspace_size(d["batch"], d["q_len"], d["kv_len"], d["n_q_heads"],
+        ws = torch.zeros(max(32768, sdpa.workspace_size(d["batch"], d["q_len"], d["kv_len"], d["n_q_heads"],
                                                        d["n_kv_heads"], d["head_dim"], q.dtype,
                                                        v_head_dim=c.v.shape[3])),
                          dtype=torch.uint8, device="cuda")
@@ -329,38 +473,47 @@ def main():
 
     t_start = time.time()
     print(f"[bench] measuring {a.workload}", file=sys.stderr, flush=True)
-    prim = measure(a.workload, a.steps, a.warmup)
-    secondary = {}
+    prim = measure(a.workload, a.steps, a.warmup, a.eager)
+    results = {a.workload: prim}
     if not a.no_secondary:
         for name in WORKLOADS:
             if name == a.workload:
                 continue
-            st = a.steps if WORKLOADS[name]["kind"] in ("decode", "tiny") else max(5, min(a.steps, 20))
+            st = a.steps if WORKLOADS[name]["kind"] in ("decode", "tiny", "decode_dv") else max(5, min(a.steps, 20))
             print(f"[bench] measuring {name}", file=sys.stderr, flush=True)
-            r = measure(name, st, max(2, min(a.warmup, 5)))
-            secondary[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "eager_ms_per_step",
-                                                 "kernel_ms", "combine_ms", "kernel_rate", "rate_unit",
-                                                 "peak", "frac", "route")}
-            secondary[name]["traffic"] = load_traffic(name)
-    cpu = None
-    if not a.no_cpu:
-        print("[bench] oracle CPU baseline", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(a.workload, a.cpu_seconds)
+            results[name] = measure(name, st, max(2, min(a.warmup, 5)), a.eager)
+    print("[bench] streaming-read ceiling", file=sys.stderr, flush=True)
+    ceil = ceiling(int(prim["roofline"]["work_per_launch"]), a.steps) if prim["unit"] == "GB/s" else None
 
-    roof = {"bound": prim["bound"], "achieved": prim["kernel_rate"], "peak": prim["peak"],
-            "unit": prim["rate_unit"], "frac": prim["frac"], "traffic": load_traffic(a.workload),
-            "kernel_ms": prim["kernel_ms"], "kernel_ms_p10": prim["kernel_ms_p10"],
-            "kernel_ms_p90": prim["kernel_ms_p90"], "combine_ms": prim["combine_ms"],
-            "work_per_launch": prim["work"], "work_unit": prim["work_unit"]}
+    cpu, cpus = None, {}
+    if not a.no_cpu:
+        import concurrent.futures as cf
+        import multiprocessing as mp
+        cores = min(len(os.sched_getaffinity(0)), MAX_POOL)
+        names = [n for n in CPU_WORKLOADS if n in results] or [a.workload]
+        if a.workload not in names:
+            names.insert(0, a.workload)
+        with cf.ProcessPoolExecutor(cores, mp_context=mp.get_context("spawn")) as pool:
+            for n in names:
+                print(f"[bench] oracle CPU baseline {n}", file=sys.stderr, flush=True)
+                cpus[n] = cpu_baseline(n, a.cpu_seconds, pool, cores)
+        cpu = cpus[a.workload]
+
+    def entry(r):
+        return {k: r[k] for k in ("value", "unit", "ms_per_step", "eager_ms_per_step", "route", "roofline")}
+
     line = {
         "metric": METRIC, "value": prim["value"], "unit": prim["unit"], "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": prim["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": prim["config"]["dtype"], "data": "synthetic (seeded, see sdpa_inputs.py)",
         "config": prim["config"], "eager_ms_per_step": prim["eager_ms_per_step"],
-        "timing": "HIP graph of K steps, replayed" if prim["graph_ms_per_step"] else "eager",
-        "cold_cache_replicas": prim["replicas"], "route": prim["route"], "roofline": roof,
-        "cpu_baseline": cpu, "secondary": secondary, "kernel_hash": kernel_hash(a.workload),
-        "wall_s": round(time.time() - t_start, 1),
+        "timing": "HIP graph of K steps: one untimed replay, one replay timed with HIP events",
+        "cold_cache_replicas": prim["replicas"], "route": prim["route"], "roofline": prim["roofline"],
+        "prefill": {n: entry(results[n]) for n in PREFILL if n in results},
+        "ceiling": ceil, "cpu_baseline": cpu,
+        "cpu_baselines": cpus,
+        "secondary": {n: entry(r) for n, r in results.items() if n != a.workload and n not in PREFILL},
+        "kernel_hash": kernel_hash(a.workload), "wall_s": round(time.time() - t_start, 1),
     }
     print(json.dumps(line), flush=True)
 

@@ -143,11 +143,16 @@ typedef struct {
  *                  SDPA_BF16, any of them for any dtype) and BOOLEAN
  *                  (mask_dtype = SDPA_U8); mask must then be non-null.
  *   workspace      device scratch of at least sdpa_workspace_size(...) bytes,
- *                  256-byte aligned (may be NULL when that size is 0).  The
- *                  vector kernel writes its per-split partial results there
- *                  and reads them back within the same call; the contents
- *                  need no initialisation and are garbage afterwards.  Calls
- *                  that share a workspace must be ordered on one stream.
+ *                  256-byte aligned (may be NULL when that size is 0), not
+ *                  overlapping q, k, v, out or the mask.  The vector kernel
+ *                  splits the keys over several workgroups (the 2-pass vector
+ *                  kernel of mlx issue #3885, "Current routing") and keeps
+ *                  their partial results there.  Its first 32768 bytes are
+ *                  arrival counters: they must be ZERO before the first call
+ *                  that uses the workspace (allocate it zero-filled once) and
+ *                  every call leaves them zero again; the rest needs no
+ *                  initialisation and is garbage afterwards.  Calls that
+ *                  share a workspace must be ordered on one stream.
  *   stream         hipStream_t as void*.
  * Returns SDPA_OK or a negative status; nothing is enqueued on error.
  */
@@ -261,11 +266,15 @@ int sdpa_describe_route_ex(int batch, int q_len, int kv_len, int n_q_heads, int 
                            char* buf, size_t len);
 
 /*
- * sdpa_workspace_size -- bytes of workspace sdpa_forward needs for this shape:
- * 0 for the full kernel; for the vector kernel the per-split partial results
- * (an fp32 output row plus running max and sum, per split, query head and
- * query row).  Returns 0 for unsupported shapes as well.  The mask kind does
- * not change the size.
+ * sdpa_workspace_size -- bytes of workspace sdpa_forward needs for this shape
+ * (the 2-pass vector kernel of mlx issue #3885, "Current routing", keeps one
+ * partial result per key split): 0 for the full kernel and for a vector call
+ * whose key range is not split; otherwise 32768 bytes of arrival counters
+ * (zero-initialised once, see sdpa_forward) followed by the per-split partial
+ * results (an fp32 output row plus running max and sum, per split, query head
+ * and query row).  An upper bound over every mask kind, mask layout, sliding
+ * window and rotary option for the same shape, on the current device.
+ * Returns 0 for unsupported shapes as well.
  */
 size_t sdpa_workspace_size(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads,
                            int head_dim, sdpa_dtype dtype);
@@ -274,10 +283,16 @@ size_t sdpa_workspace_size(int batch, int q_len, int kv_len, int n_q_heads, int 
 size_t sdpa_workspace_size_ex(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads,
                               int head_dim, int v_head_dim, sdpa_dtype dtype);
 
-/* sdpa_head_dims -- writes up to n built head dims (ascending) to out; returns how many exist. */
+/* sdpa_head_dims -- writes up to n built head dims (ascending) to out; returns how many exist.
+ * Part of the queryable answer to "which shapes have a fused kernel" that mlx
+ * issue #3885 asks for under "Requests" (head dims as template parameters,
+ * not an enumerated list discovered by a silent fallback). */
 int sdpa_head_dims(int* out, int n);
 
-/* sdpa_strerror -- static description of a status code (never NULL). */
+/* sdpa_strerror -- static description of a status code (never NULL).  Every
+ * refusal is a status the caller sees: mlx issue #3885 (the comments after
+ * "Requests") shows an unchecked launch returning silent zeros and turns it
+ * into a loud error; here no call falls back or fails silently. */
 const char* sdpa_strerror(int status);
 
 /* sdpa_last_hip_error -- the hipError_t of the last SDPA_EHIP on this thread (0 if none). */
@@ -286,7 +301,10 @@ int sdpa_last_hip_error(void);
 /*
  * sdpa_route_counters -- diagnostics: copies up to n counters into out and
  * returns how many exist: [0] calls, [1] full launches, [2] vector launches,
- * [3] rejected (any error status).  calls == full + vector + rejected.
+ * [3] rejected (any error status).  calls == full + vector + rejected.  The
+ * counters are relaxed atomics, as the per-route hit / fallback counters of
+ * the commits merged in mlx PR #4330 (their C diagnostics ABI and the
+ * invariant attempts == hits + fallbacks).
  */
 int sdpa_route_counters(uint64_t* out, int n);
 
@@ -305,6 +323,19 @@ int sdpa_route_counters(uint64_t* out, int n);
  */
 int sdpa_timing_start(int max_calls);
 int sdpa_timing_stop(float* ms, int cap);
+
+/*
+ * sdpa_probe_stream_read -- diagnostics, not attention: one launch of a plain
+ * streaming read of `bytes` bytes at device address `src` (16-byte aligned,
+ * bytes a multiple of 16), one 256-thread workgroup per CU, on `stream`.
+ * Decode is bound by reading K and V once (mlx issue #3885, "Measured
+ * impact": decode time follows the K/V bytes); this kernel reads the same
+ * amount with nothing else to do, which is the practical ceiling a launch of
+ * that size reaches.  `sink` is a 4-byte device word that is written only for
+ * one specific data pattern (it keeps the reads from being optimised away).
+ * Returns SDPA_OK, SDPA_EINVAL or SDPA_EHIP.
+ */
+int sdpa_probe_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     forward,
     head_dims,
     kernel_timing,
+    probe_stream_read,
     load,
     rope,
     route_counters,

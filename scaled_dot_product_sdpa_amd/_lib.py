@@ -29,7 +29,7 @@ EXPORTS = ("sdpa_forward", "sdpa_forward_sliding", "sdpa_forward_ex", "sdpa_rope
            "sdpa_select_kernel_ex", "sdpa_describe_route", "sdpa_describe_route_ex", "sdpa_workspace_size",
            "sdpa_workspace_size_ex",
            "sdpa_head_dims", "sdpa_strerror", "sdpa_last_hip_error", "sdpa_route_counters",
-           "sdpa_timing_start", "sdpa_timing_stop")
+           "sdpa_timing_start", "sdpa_timing_stop", "sdpa_probe_stream_read")
 
 
 class Strides(ctypes.Structure):
@@ -98,6 +98,8 @@ def load(path: str = LIB_PATH):
         lib.sdpa_timing_start.restype = i
         lib.sdpa_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_float), i]
         lib.sdpa_timing_stop.restype = i
+        lib.sdpa_probe_stream_read.argtypes = [vp, sz, vp, vp]
+        lib.sdpa_probe_stream_read.restype = i
         _lib = lib
         return lib
 
@@ -186,6 +188,14 @@ class kernel_timing:
         return False
 
 
+def probe_stream_read(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """One launch of the library's plain streaming read over src's bytes (diagnostics)."""
+    st = load().sdpa_probe_stream_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
+                                       torch.cuda.current_stream(src.device).cuda_stream)
+    if st != 0:
+        raise SdpaError(st, "sdpa_probe_stream_read")
+
+
 def _as_code(dtype) -> int:
     return dtype if isinstance(dtype, int) else dtype_code(dtype)
 
@@ -211,7 +221,8 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        # zero-filled once: its leading arrival words must start at zero (every call leaves them zero)
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 

@@ -64,6 +64,7 @@ struct Params {
     int kbase;        // decode: first key of split 0 (keys before it are masked for every row)
     int window;       // MASK_SLIDE: keys per query (>= 1)
     int pairs;        // prefill, causal: a workgroup takes row tiles t and last - t
+    int nx;           // XCD count of the device: workgroup i runs on XCD i % nx
     // rotary embedding of Q (0 = none): columns [0, rope_dim) of query row i
     // turn by the table angles of position rope_pos0 + i ([n_pos][rope_dim / 2] fp32)
     int rope_dim;
@@ -221,6 +222,28 @@ __device__ __forceinline__ float sum_x32(float x) { const f32x2_t r = pair32(x);
 __device__ __forceinline__ float max_x16(float x) { const f32x2_t r = pair16(x); return fmaxf(r[0], r[1]); }
 __device__ __forceinline__ float sum_x16(float x) { const f32x2_t r = pair16(x); return r[0] + r[1]; }
 
+// max / sum over all 64 lanes of a wave, the result in every lane: quad
+// exchanges and row mirrors (DPP) reduce each 16-lane row, then the two lane
+// swaps above combine the rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+    x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+    x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
+    x = fmaxf(x, dpp_mov<0x140>(x));  // row_mirror
+    return max_x32(max_x16(x));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    x += dpp_mov<0x141>(x);
+    x += dpp_mov<0x140>(x);
+    return sum_x32(sum_x16(x));
+}
+
 // ---------------------------------------------------------------------------
 // Masks are read in groups of 4 consecutive keys (the 4 keys one lane holds
 // per accumulator group).  Raw form kept in registers until use:
@@ -308,5 +331,14 @@ __device__ __forceinline__ float mask_value(const typename MaskRaw<MASK>::type& 
         return (float)bitcast<_Float16>((uint16_t)h);
     }
 }
+
+// Geometry of the single-launch decode kernel (decode_fused_kernel.h).
+struct FusedGeom {
+    int nx;      // XCD count (grid stride of one group's splits)
+    int groups;  // G = B * Hkv * col_groups * VS
+    int splits;  // S
+    int nblk;    // 16-key blocks of the keys every group reads (from kbase)
+    int rv;      // rows per group partial (min(16, n_rep * Lq))
+};
 
 }  // namespace sdpa_dev

@@ -26,8 +26,9 @@
 //     are zero-padded in LDS and in the Q fragments; when D % 32 != 0 the V^T
 //     tile has spare rows and row D is set to ones, so the MFMA produces the
 //     softmax row sums along with O (already rescaled with it).
-//   * Prefill grid: one dimension, 8 x ceil(items / 8) workgroups, items =
-//     (batch, query head, query tile).  Workgroup i runs on XCD i % 8, so
+//   * Prefill grid: one dimension, NX x ceil(items / NX) workgroups (NX = the
+//     device's XCD count), items = (batch, query head, query tile).
+//     Workgroup i runs on XCD i % NX, so
 //     XCD x is given the contiguous item range [x * per, (x + 1) * per): the
 //     query tiles of one head run on one XCD and share its L2 copy of that
 //     head's K/V.  Causal items run longest-first and stop at the diagonal
@@ -102,8 +103,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void attn_tile_kernel(const Params p
     if constexpr (!DECODE) {
         const int nqt = (p.Lq + BM - 1) / BM;
         const int total = nqt * p.Hq * p.B;
-        const int per = (total + 7) / 8;
-        const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+        const int per = (total + p.nx - 1) / p.nx;
+        const int item = (int)(blockIdx.x % p.nx) * per + (int)(blockIdx.x / p.nx);
         if (item >= total) return;  // whole workgroup: no barrier is skipped
         const int tt = item % nqt, bh = item / nqt;
         qh = bh % p.Hq;

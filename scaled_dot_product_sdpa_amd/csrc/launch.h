@@ -11,6 +11,7 @@ namespace sdpa_host {
 using sdpa_dev::Params;
 
 typedef hipError_t (*launch_fn)(const Params&, dim3 grid, hipStream_t stream);
+typedef hipError_t (*fused_fn)(const Params&, const sdpa_dev::FusedGeom&, dim3 grid, hipStream_t stream);
 
 struct TileInfo {
     int bn;   // keys per tile (decode: keys per chunk; a split is a whole number of chunks)
@@ -41,19 +42,23 @@ struct KernelSet {
     // handles both layouts)
     launch_fn full_strided[sdpa_dev::MASK_VARIANTS];
     launch_fn full_strided_rope[sdpa_dev::MASK_VARIANTS];
+    // 16-bit decode in one launch (split keys merged in L2 by the last
+    // workgroup of each group), by V column slices (index VS - 1; null where
+    // not built) and mask variant
+    fused_fn decode_fused[2][sdpa_dev::MASK_VARIANTS];
+    fused_fn decode_fused_rope[2][sdpa_dev::MASK_VARIANTS];
+    int fused_nt[2];  // threads per workgroup of those kernels, by V slices
 };
 
 // Returns hipErrorInvalidConfiguration when the compiled kernel cannot run
 // `nt` threads per workgroup (register or LDS limits): such a launch would be
-// dropped by the hardware, so it is refused before it is made.
+// dropped by the hardware, so it is refused before it is made.  Callers keep
+// the result in a function-local static (initialised once, thread-safe).
 template <class K>
-hipError_t check_launch_once(K kernel, int nt, hipError_t* cache, bool* done) {
-    if (*done) return *cache;
+hipError_t check_launch(K kernel, int nt) {
     hipFuncAttributes a;
     hipError_t e = hipFuncGetAttributes(&a, reinterpret_cast<const void*>(kernel));
     if (e == hipSuccess && a.maxThreadsPerBlock < nt) e = hipErrorInvalidConfiguration;
-    *cache = e;
-    *done = true;
     return e;
 }
 

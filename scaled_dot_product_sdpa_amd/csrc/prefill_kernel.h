@@ -88,8 +88,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     const int nqt = (p.Lq + BM - 1) / BM;
     const int nit = pairs ? (nqt + 1) / 2 : nqt;  // row-tile items per head
     const int total = nit * p.Hq * p.B;
-    const int per = (total + 7) / 8;
-    const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    const int per = (total + p.nx - 1) / p.nx;
+    const int item = (int)(blockIdx.x % p.nx) * per + (int)(blockIdx.x / p.nx);
     if (item >= total) return;
     // With a mask tensor, the heads of one row tile run next to each other on one
     // XCD so its mask rows (usually shared by every head) are read from L2;

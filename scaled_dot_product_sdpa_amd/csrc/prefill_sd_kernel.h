@@ -91,8 +91,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void prefill_sd_kernel(const Params 
     const int nit = pairs ? (nrt + 1) / 2 : nrt;  // row-tile items per head group
     const int nhg = n_rep / HG;
     const int total = nit * nhg * p.Hkv * p.B;
-    const int per = (total + 7) / 8;
-    const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    const int per = (total + p.nx - 1) / p.nx;
+    const int item = (int)(blockIdx.x % p.nx) * per + (int)(blockIdx.x / p.nx);
     if (item >= total) return;
     // with a mask tensor the head groups of one row tile run next to each other
     // (mask rows shared through L2), otherwise the row tiles of one group do

@@ -21,8 +21,10 @@
 #include <vector>
 
 #include "attn_kernel.h"
+#include "decode_fused_kernel.h"
 #include "launch.h"
 #include "rope_kernel.h"
+#include "stream_probe.h"
 
 using sdpa_dev::Params;
 using sdpa_host::KernelSet;
@@ -31,8 +33,32 @@ using sdpa_host::launch_fn;
 namespace {
 
 constexpr int kVectorMaxQLen = 8;     // qL <= 8 -> vector kernel
-constexpr int kDeviceCUs = 256;       // MI355X compute units (grid heuristics only)
 constexpr int kMaxGridYZ = 65535;
+constexpr int kMaxDevices = 64;
+
+// Compute units and XCDs of the current device (grid heuristics and the XCD
+// mapping of workgroups), queried once per device.  Without a device (host
+// only queries) an MI355X is assumed: 256 CUs in 8 XCDs.
+struct DevInfo {
+    int cus;
+    int nx;
+};
+DevInfo device_info() {
+    static std::atomic<uint64_t> cache[kMaxDevices];  // (cus << 32 | nx), 0 = not queried yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DevInfo{256, 8};
+    uint64_t v = cache[dev].load(std::memory_order_acquire);
+    if (v == 0) {
+        int cus = 0, nx = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipDeviceGetAttribute(&nx, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || nx <= 0 || nx > 16)
+            nx = 1;
+        v = ((uint64_t)cus << 32) | (uint64_t)nx;
+        cache[dev].store(v, std::memory_order_release);
+    }
+    return DevInfo{(int)(v >> 32), (int)(v & 0xffffffffu)};
+}
 
 std::atomic<uint64_t> g_counters[4];  // calls, full, vector, rejected
 thread_local int g_last_hip_error = 0;
@@ -124,6 +150,23 @@ struct DecodePlan {
 
 // Split the key axis so the decode grid covers the chip about twice; a
 // test-only environment override (SDPA_DECODE_SPLITS) pins the count.
+// The split count never exceeds split_cap(kv_len), which grows with kv_len:
+// the workspace is sized with it (a sliding window plans over fewer keys).
+long split_cap(int batch, int q_len, int kv_len, int hq, int hkv, const sdpa_host::TileInfo& t, int cus) {
+    const int rows = (hq / hkv) * q_len;
+    const long groups = (long)batch * hkv * ((rows + t.cols - 1) / t.cols);
+    const int max_splits = (kv_len + t.bn - 1) / t.bn;
+    long s = (2L * cus + groups - 1) / groups;
+    if (const char* env = std::getenv("SDPA_DECODE_SPLITS")) {
+        const long v = std::strtol(env, nullptr, 10);
+        if (v > 0) s = v;
+    }
+    if (s < 1) s = 1;
+    if (s > max_splits) s = max_splits;
+    if (s > sdpa_dev::kMaxSplits) s = sdpa_dev::kMaxSplits;
+    return s;
+}
+
 DecodePlan decode_plan(int batch, int q_len, int kv_len, int hq, int hkv, const sdpa_host::TileInfo& t) {
     DecodePlan p;
     const int rows = (hq / hkv) * q_len;
@@ -131,7 +174,7 @@ DecodePlan decode_plan(int batch, int q_len, int kv_len, int hq, int hkv, const 
     p.col_groups = (rows + cols - 1) / cols;
     const long groups = (long)batch * hkv * p.col_groups;
     const int max_splits = (kv_len + t.bn - 1) / t.bn;
-    long s = (2L * kDeviceCUs + groups - 1) / groups;
+    long s = (2L * device_info().cus + groups - 1) / groups;
     if (const char* env = std::getenv("SDPA_DECODE_SPLITS")) {
         const long v = std::strtol(env, nullptr, 10);
         if (v > 0) s = v;
@@ -147,9 +190,78 @@ DecodePlan decode_plan(int batch, int q_len, int kv_len, int hq, int hkv, const 
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t decode_ws_bytes(int batch, int q_len, int hq, int d, const DecodePlan& p) {
+// Every decode workspace starts with kFusedCounterWords arrival words of the
+// single-launch kernel (zero before and after every call); the split + combine
+// kernels place their partial results after them and never touch them.
+constexpr size_t kCounterBytes = (size_t)sdpa_dev::kFusedCounterWords * 4;
+
+// (a single split of the 16-bit split kernel writes the output itself: no workspace)
+size_t decode_ws_bytes(int batch, int q_len, int hq, int d, long splits, sdpa_dtype dt) {
+    if (splits == 1 && dt != SDPA_F32) return 0;
     const size_t rows = (size_t)batch * hq * q_len;
-    return align256(rows * p.splits * d * sizeof(float)) + align256(rows * p.splits * 2 * sizeof(float));
+    return kCounterBytes + align256(rows * splits * d * sizeof(float)) + align256(rows * splits * 2 * sizeof(float));
+}
+
+// Single-launch decode (16-bit): groups of (batch, kv head, column group of
+// <= 16 rows, V column slice) whose splits all run on one XCD.  Taken when the
+// groups spread evenly over the XCDs (with two V slices if that is what it
+// takes); otherwise the split + combine kernels run.
+struct FusedPlan {
+    bool use = false;
+    int vs = 1;       // V column slices
+    int groups = 0;   // G
+    int splits = 1;   // S
+    int nblk = 0;     // 16-key blocks from kbase
+    int rv = 0;       // rows per partial
+    int col_groups = 0;
+};
+constexpr int kFusedKeys = 16;  // keys per block of the single-launch kernel
+
+FusedPlan fused_plan(const KernelSet* ks, int batch, int q_len, int kv_len_eff, int hq, int hkv, int dv, int rope,
+                     int variant, bool mask_ok = true) {
+    FusedPlan f;
+    if (!ks || !ks->fused_nt[0] || !mask_ok) return f;
+    const DevInfo di = device_info();
+    const int nx = di.nx;
+    const int rows = (hq / hkv) * q_len;
+    f.col_groups = (rows + 15) / 16;
+    f.rv = rows < 16 ? rows : 16;
+    const long g1 = (long)batch * hkv * f.col_groups;
+    auto built = [&](int vs) {
+        return (rope ? ks->decode_fused_rope[vs - 1][variant] : ks->decode_fused[vs - 1][variant]) != nullptr;
+    };
+    int vs = 0;
+    if (g1 % nx == 0 && built(1)) vs = 1;
+    else if ((2 * g1) % nx == 0 && built(2) && dv % 32 == 0) vs = 2;
+    if (!vs) return f;
+    const long G = g1 * vs;
+    if (G > (1L << 30)) return f;
+    f.vs = vs;
+    f.groups = (int)G;
+    f.nblk = (kv_len_eff + kFusedKeys - 1) / kFusedKeys;
+    // one workgroup per CU: S splits per group
+    long s = (long)di.cus / G;
+    const long by_keys = f.nblk / 2;  // at least two 16-key blocks per split
+    if (s > by_keys) s = by_keys;
+    if (const char* env = std::getenv("SDPA_DECODE_SPLITS")) {
+        const long v = std::strtol(env, nullptr, 10);
+        if (v > 0) s = v;
+    }
+    if (s > sdpa_dev::kFusedMaxSplits) s = sdpa_dev::kFusedMaxSplits;
+    if (s > f.nblk) s = f.nblk;
+    if (s < 1) s = 1;
+    // block indices are computed in 32-bit arithmetic; merged groups need an arrival word each
+    if ((long long)f.nblk * s >= (1LL << 31)) return FusedPlan{};
+    if (s > 1 && G > sdpa_dev::kFusedMaxGroups) return FusedPlan{};
+    f.splits = (int)s;
+    f.use = true;
+    return f;
+}
+
+size_t fused_ws_bytes(const FusedPlan& f, int dv) {
+    if (f.splits == 1) return 0;
+    const size_t slots = (size_t)f.groups * f.splits * f.rv;
+    return kCounterBytes + align256(slots * (dv / f.vs) * sizeof(float)) + align256(slots * 2 * sizeof(float));
 }
 
 // Byte extent of a strided tensor: [base, base + span).
@@ -220,7 +332,7 @@ FullGrid full_grid(const sdpa_host::TileInfo& t, bool causal, int batch, int q_l
     const int bm = t.cols / hg;
     const long qtiles = (q_len + bm - 1) / bm;
     const long groups = (long)(n_q_heads / hg) * batch;
-    if (t.causal_pairs && causal && (qtiles + 1) / 2 * groups >= kDeviceCUs) return FullGrid{(qtiles + 1) / 2 * groups, 1};
+    if (t.causal_pairs && causal && (qtiles + 1) / 2 * groups >= device_info().cus) return FullGrid{(qtiles + 1) / 2 * groups, 1};
     return FullGrid{qtiles * groups, 0};
 }
 
@@ -237,9 +349,16 @@ FullPlan full_plan(const KernelSet* ks, int variant, int batch, int q_len, int n
     FullPlan fp{&ks->full_cfg, full_grid(ks->full_cfg, causal, batch, q_len, n_q_heads, n_kv_heads), false};
     if (causal && !fp.grid.pairs && ks->full_small[variant]) {
         const FullGrid gs = full_grid(ks->full_small_cfg, causal, batch, q_len, n_q_heads, n_kv_heads);
-        if (gs.pairs || fp.grid.items < kDeviceCUs) fp = FullPlan{&ks->full_small_cfg, gs, true};
+        if (gs.pairs || fp.grid.items < device_info().cus) fp = FullPlan{&ks->full_small_cfg, gs, true};
     }
     return fp;
+}
+
+// Kernel mask variant of a mask kind (additive splits by mask element width).
+int kernel_variant(sdpa_mask_kind mk, sdpa_dtype mask_dtype) {
+    if (mk == SDPA_MASK_ADDITIVE) return mask_dtype == SDPA_F32 ? sdpa_dev::MASK_ADD32 : sdpa_dev::MASK_ADD16;
+    if (mk == SDPA_MASK_SLIDING) return sdpa_dev::MASK_SLIDE;
+    return (int)mk;
 }
 
 std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int d, int dv, sdpa_dtype dt,
@@ -267,12 +386,22 @@ std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int 
                       t.lds, fg.items, fg.pairs ? " causal-pairs" : "");
     } else {
         const auto& t = ks->dec_cfg;
-        DecodePlan p = decode_plan(batch, q_len, kv_len, hq, hkv, t);
-        std::snprintf(buf, sizeof buf,
-                      "vector %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d splits=%d keys/split=%d colgroups=%d "
-                      "cols=%d threads=%d lds=%d",
-                      dtype_name(dt), dn, mask_name(mk), batch, q_len, kv_len, hq, hkv, p.splits, p.keys_per_split,
-                      p.col_groups, t.cols, t.nt, t.lds);
+        const FusedPlan f = fused_plan(ks, batch, q_len, kv_len, hq, hkv, dv, 0, kernel_variant(mk, SDPA_BF16));
+        if (f.use) {
+            std::snprintf(buf, sizeof buf,
+                          "vector-fused %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d groups=%d vslices=%d splits=%d "
+                          "blocks/split=%d colgroups=%d threads=%d xcds=%d",
+                          dtype_name(dt), dn, mask_name(mk), batch, q_len, kv_len, hq, hkv, f.groups, f.vs, f.splits,
+                          (f.nblk + f.splits - 1) / f.splits, f.col_groups, ks->fused_nt[f.vs - 1],
+                          device_info().nx);
+        } else {
+            DecodePlan p = decode_plan(batch, q_len, kv_len, hq, hkv, t);
+            std::snprintf(buf, sizeof buf,
+                          "vector %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d splits=%d keys/split=%d colgroups=%d "
+                          "cols=%d threads=%d lds=%d",
+                          dtype_name(dt), dn, mask_name(mk), batch, q_len, kv_len, hq, hkv, p.splits,
+                          p.keys_per_split, p.col_groups, t.cols, t.nt, t.lds);
+        }
     }
     return buf;
 }
@@ -356,8 +485,24 @@ size_t sdpa_workspace_size_ex(int batch, int q_len, int kv_len, int n_q_heads, i
         k != SDPA_KERNEL_VECTOR)
         return 0;
     const KernelSet* ks = kernel_set(dtype, head_dim, v_head_dim);
-    const DecodePlan p = decode_plan(batch, q_len, kv_len, n_q_heads, n_kv_heads, ks->dec_cfg);
-    return decode_ws_bytes(batch, q_len, n_q_heads, v_head_dim, p);
+    // an upper bound over every mask kind, window and rotary option: the
+    // single-launch plan (its split count only grows with the key count), and
+    // the split + combine plan's largest split count
+    size_t need = 0;
+    for (int rope = 0; rope < 2; ++rope)
+        for (int var = 0; var < sdpa_dev::MASK_VARIANTS; ++var) {
+            // (a mask tensor without aligned 4-key runs takes the split + combine kernels)
+            const FusedPlan f = fused_plan(ks, batch, q_len, kv_len, n_q_heads, n_kv_heads, v_head_dim, rope, var);
+            const size_t bf = f.use ? fused_ws_bytes(f, v_head_dim) : 0;
+            const size_t bs = decode_ws_bytes(batch, q_len, n_q_heads, v_head_dim,
+                                              split_cap(batch, q_len, kv_len, n_q_heads, n_kv_heads, ks->dec_cfg,
+                                                        device_info().cus),
+                                              dtype);
+            const bool tensor = var == sdpa_dev::MASK_ADD16 || var == sdpa_dev::MASK_ADD32 || var == sdpa_dev::MASK_BOOL;
+            const size_t b = (f.use && !tensor) ? bf : (bf > bs ? bf : bs);
+            if (b > need) need = b;
+        }
+    return need;
 }
 
 size_t sdpa_workspace_size(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads, int head_dim,
@@ -430,6 +575,8 @@ int sdpa_route_counters(uint64_t* out, int n) {
     return 4;
 }
 
+}  // extern "C"
+
 namespace {
 
 int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
@@ -460,9 +607,8 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         (double)kv_len * (double)(v_st.l > 0 ? v_st.l : 1) * es >= 4294967296.0)
         return reject(SDPA_EUNSUPPORTED);
     const size_t oq = span_bytes(no, o_st, es);
-    if (overlaps(out, oq, q, span_bytes(nq, q_st, es)) || overlaps(out, oq, k, span_bytes(nk, k_st, es)) ||
-        overlaps(out, oq, v, span_bytes(nv, v_st, es)))
-        return reject(SDPA_EINVAL);
+    const size_t sq = span_bytes(nq, q_st, es), sk = span_bytes(nk, k_st, es), sv = span_bytes(nv, v_st, es);
+    if (overlaps(out, oq, q, sq) || overlaps(out, oq, k, sk) || overlaps(out, oq, v, sv)) return reject(SDPA_EINVAL);
 
     Params p{};
     int mvec = 0;
@@ -485,6 +631,7 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         p.mask = mask;
         const int64_t mn[4] = {batch, n_q_heads, q_len, kv_len};
         p.mask_span = (int64_t)span_bytes(mn, mask_st, mes);
+        if (overlaps(out, oq, mask, (size_t)p.mask_span)) return reject(SDPA_EINVAL);
         p.ms[0] = mask_st.b;
         p.ms[1] = mask_st.h;
         p.ms[2] = mask_st.l;
@@ -521,6 +668,8 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         if (!q_rope->cos || !q_rope->sin || q_pos0 < 0 || (long)q_pos0 + q_len > (long)q_rope->n_pos)
             return reject(SDPA_EINVAL);
         if (((uintptr_t)q_rope->cos) % 16 != 0 || ((uintptr_t)q_rope->sin) % 16 != 0) return reject(SDPA_EUNSUPPORTED);
+        const size_t tb = (size_t)q_rope->n_pos * (size_t)(r / 2) * sizeof(float);
+        if (overlaps(out, oq, q_rope->cos, tb) || overlaps(out, oq, q_rope->sin, tb)) return reject(SDPA_EINVAL);
         p.rope_dim = r;
         p.rope_pos0 = q_pos0;
         p.rope_cos = q_rope->cos;
@@ -529,10 +678,9 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
 
     const KernelSet* ks = kernel_set(dtype, head_dim, v_head_dim);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // kernel mask variant: the additive kind splits by mask element width
-    int mk = (int)mask_kind;
-    if (mask_kind == SDPA_MASK_ADDITIVE) mk = (mask_dtype == SDPA_F32) ? sdpa_dev::MASK_ADD32 : sdpa_dev::MASK_ADD16;
-    if (mask_kind == SDPA_MASK_SLIDING) mk = sdpa_dev::MASK_SLIDE;
+    const int mk = kernel_variant(mask_kind, mask_dtype);
+    const DevInfo di = device_info();
+    p.nx = di.nx;
     // optional per-kernel timing (diagnostics): events bracket each launch on `s`
     int tcall = -1;
     if (g_timing.used < g_timing.armed) tcall = g_timing.used++;
@@ -548,7 +696,7 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         p.pairs = fp.grid.pairs;
         const long items = fp.grid.items;
         if (items > (1L << 30)) return reject(SDPA_EUNSUPPORTED);
-        dim3 grid((unsigned)(8 * ((items + 7) / 8)), 1, 1);
+        dim3 grid((unsigned)(di.nx * ((items + di.nx - 1) / di.nx)), 1, 1);
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
                                     mask_kind, st, kern, reason));
         const bool strided = !p.mask_vec && ks->full_strided[mk];
@@ -572,16 +720,57 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         const long lo = (long)(kv_len - q_len) - window + 1;
         p.kbase = lo > 0 ? (int)lo : 0;
     }
+    // the single-launch kernel reads mask tensors in aligned 4-key vectors with 32-bit offsets
+    const bool mask_ok = !p.mask || (p.mask_vec && p.mask_span < (int64_t)0xffffffffLL);
+    const FusedPlan fpl = fused_plan(ks, batch, q_len, kv_len - p.kbase, n_q_heads, n_kv_heads, v_head_dim,
+                                     p.rope_dim > 0, mk, mask_ok);
+    if (fpl.use) {
+        const size_t need = fused_ws_bytes(fpl, v_head_dim);
+        if (need && (!workspace || workspace_bytes < need)) return reject(SDPA_EWORKSPACE);
+        if (need && ((uintptr_t)workspace) % 256 != 0) return reject(SDPA_EINVAL);
+        if (need && (overlaps(out, oq, workspace, need) || overlaps(q, sq, workspace, need) ||
+                     overlaps(k, sk, workspace, need) || overlaps(v, sv, workspace, need) ||
+                     (p.mask && overlaps(p.mask, (size_t)p.mask_span, workspace, need))))
+            return reject(SDPA_EINVAL);
+        const size_t slots = (size_t)fpl.groups * fpl.splits * fpl.rv;
+        p.ws_o = reinterpret_cast<float*>(workspace);
+        p.ws_ml = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kCounterBytes +
+                                                  align256(slots * (v_head_dim / fpl.vs) * sizeof(float)))
+                       : nullptr;
+        p.col_groups = fpl.col_groups;
+        sdpa_dev::FusedGeom fg{di.nx, fpl.groups, fpl.splits, fpl.nblk, fpl.rv};
+        // test-only: another XCD stride scatters a group's splits over several XCDs,
+        // which the kernel must detect (and recompute the group)
+        if (const char* env = std::getenv("SDPA_FUSED_XCD_STRIDE")) {
+            const long v = std::strtol(env, nullptr, 10);
+            if (v > 0 && fpl.groups % v == 0) fg.nx = (int)v;
+        }
+        log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
+                                    mask_kind, st, kern, reason));
+        const sdpa_host::fused_fn f = p.rope_dim > 0 ? ks->decode_fused_rope[fpl.vs - 1][mk]
+                                                     : ks->decode_fused[fpl.vs - 1][mk];
+        if (!f) return reject(SDPA_EUNSUPPORTED);
+        mark(0);
+        st = hip_status(f(p, fg, dim3((unsigned)(fpl.groups * fpl.splits)), s));
+        if (st != SDPA_OK) return reject(st);
+        mark(1);
+        g_counters[2].fetch_add(1, std::memory_order_relaxed);
+        return SDPA_OK;
+    }
     const DecodePlan plan = decode_plan(batch, q_len, kv_len - p.kbase, n_q_heads, n_kv_heads, t);
-    const size_t need = decode_ws_bytes(batch, q_len, n_q_heads, v_head_dim, plan);
-    if (!workspace || workspace_bytes < need) return reject(SDPA_EWORKSPACE);
-    if (((uintptr_t)workspace) % 256 != 0) return reject(SDPA_EINVAL);
-    if (overlaps(out, oq, workspace, need)) return reject(SDPA_EINVAL);
+    const size_t need = decode_ws_bytes(batch, q_len, n_q_heads, v_head_dim, plan.splits, dtype);
+    if (need && (!workspace || workspace_bytes < need)) return reject(SDPA_EWORKSPACE);
+    if (need && ((uintptr_t)workspace) % 256 != 0) return reject(SDPA_EINVAL);
+    if (need && (overlaps(out, oq, workspace, need) || overlaps(q, sq, workspace, need) ||
+                 overlaps(k, sk, workspace, need) || overlaps(v, sv, workspace, need) ||
+                 (p.mask && overlaps(p.mask, (size_t)p.mask_span, workspace, need))))
+        return reject(SDPA_EINVAL);
     if ((long)n_kv_heads * plan.col_groups > kMaxGridYZ) return reject(SDPA_EUNSUPPORTED);
     const size_t rows = (size_t)batch * n_q_heads * q_len;
-    p.ws_o = reinterpret_cast<float*>(workspace);
-    p.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                       align256(rows * plan.splits * v_head_dim * sizeof(float)));
+    p.ws_o = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kCounterBytes) : nullptr;
+    p.ws_ml = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kCounterBytes +
+                                              align256(rows * plan.splits * v_head_dim * sizeof(float)))
+                   : nullptr;
     p.splits = plan.splits;
     p.keys_per_split = plan.keys_per_split;
     p.col_groups = plan.col_groups;
@@ -606,6 +795,8 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
 }
 
 }  // namespace
+
+extern "C" {
 
 int sdpa_forward(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
                  sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len, int n_q_heads,
@@ -683,6 +874,16 @@ int sdpa_rope(const void* x, sdpa_strides x_st, void* y, sdpa_strides y_st, int 
         hipLaunchKernelGGL(sdpa_dev::rope_kernel<_Float16>, grid, dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(sdpa_dev::rope_kernel<__bf16>, grid, dim3(256), 0, s, a);
+    return hip_status(hipGetLastError());
+}
+
+int sdpa_probe_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+    if (!src || !sink || bytes == 0) return SDPA_EINVAL;
+    if (bytes % 16 != 0 || ((uintptr_t)src) % 16 != 0 || ((uintptr_t)sink) % 4 != 0) return SDPA_EINVAL;
+    const DevInfo di = device_info();
+    hipLaunchKernelGGL(sdpa_dev::stream_read_kernel, dim3((unsigned)di.cus), dim3(sdpa_dev::kProbeThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const sdpa_dev::u32x4_t*>(src),
+                       (uint64_t)(bytes / 16), reinterpret_cast<uint32_t*>(sink));
     return hip_status(hipGetLastError());
 }
 

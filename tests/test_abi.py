@@ -85,21 +85,40 @@ def test_value_head_dim_pairing(lib):
 
 
 def test_describe_route(lib):
+    # 4 kv heads over 8 XCDs: two V column slices make 8 groups, one launch
     s = sdpa.describe_route(1, 1, 4096, 32, 4, 512, 2, "additive")
-    assert s.startswith("vector bf16 d512 additive") and "splits=" in s
+    assert s.startswith("vector-fused bf16 d512 additive") and "vslices=2" in s and "splits=32" in s, s
+    s = sdpa.describe_route(1, 1, 4096, 32, 8, 256, 2, "additive")
+    assert s.startswith("vector-fused bf16 d256 additive") and "groups=8 vslices=1 splits=32" in s, s
+    # 3 kv heads do not spread evenly over the XCDs: split + combine kernels
+    s = sdpa.describe_route(1, 1, 4096, 12, 3, 128, 2, "none")
+    assert s.startswith("vector bf16 d128 none") and "splits=" in s, s
+    # float32 decode always takes the split + combine kernels
+    assert sdpa.describe_route(1, 1, 4096, 32, 8, 256, 0, "none").startswith("vector f32")
     s = sdpa.describe_route(1, 8192, 8192, 16, 16, 72, 2, "causal")
     assert s.startswith("full bf16 d72 causal")
     assert sdpa.describe_route(1, 9, 9, 8, 4, 65, 2).startswith("unsupported")
 
 
 def test_workspace_size(lib):
-    assert sdpa.workspace_size(1, 100, 100, 8, 2, 64, 2) == 0          # full kernel needs none
-    ws = sdpa.workspace_size(1, 1, 4096, 32, 4, 512, 2)
-    m = re.search(r"splits=(\d+)", sdpa.describe_route(1, 1, 4096, 32, 4, 512, 2))
-    s = int(m.group(1))
-    rows = 32
     align = lambda x: (x + 255) // 256 * 256
-    assert ws == align(rows * s * 512 * 4) + align(rows * s * 2 * 4)
+    assert sdpa.workspace_size(1, 100, 100, 8, 2, 64, 2) == 0          # full kernel needs none
+    # single-launch decode: 32 KiB of arrival words, then per (group, split, row) one
+    # fp32 partial row of the group's V columns and its (max, sum)
+    # (a mask tensor without aligned 4-key runs takes the split + combine kernels: the size covers both)
+    ws = sdpa.workspace_size(1, 1, 4096, 32, 4, 512, 2)
+    route = sdpa.describe_route(1, 1, 4096, 32, 4, 512, 2)
+    G, vs, S = (int(re.search(k + r"=(\d+)", route).group(1)) for k in ("groups", "vslices", "splits"))
+    slots = G * S * 8                                                   # 8 query heads per kv head, q_len 1
+    fused = 32768 + align(slots * (512 // vs) * 4) + align(slots * 2 * 4)
+    split_combine = 32768 + align(32 * 64 * 512 * 4) + align(32 * 64 * 2 * 4)
+    assert ws == max(fused, split_combine)
+    # split + combine: per (query row, split) one fp32 output row and (max, sum); the
+    # split count is the largest any key count up to kv_len plans
+    ws = sdpa.workspace_size(1, 1, 4096, 24, 3, 128, 2)
+    assert sdpa.describe_route(1, 1, 4096, 24, 3, 128, 2).startswith("vector bf16")
+    rows, s = 24, 64
+    assert ws == 32768 + align(rows * s * 128 * 4) + align(rows * s * 2 * 4)
     assert sdpa.workspace_size(1, 1, 4096, 32, 4, 65, 2) == 0
 
 
@@ -137,7 +156,7 @@ def test_forward_rejects_bad_arguments_before_touching_the_gpu(lib):
     assert _forward(lib, mk=2, mask=4096 * 64, mdt=2) == -1            # boolean mask must be u8
     assert _forward(lib, mk=1, mask=4096 * 64, mdt=3) == -1            # additive mask can't be u8
     assert _forward(lib, mk=7) == -1                                   # unknown mask kind
-    assert _forward(lib, o=1 << 20, dims=(1, 1, 16, 2, 2, 64), ws=None, wsb=0) == -3  # decode workspace
+    assert _forward(lib, o=1 << 21, dims=(1, 1, 4096, 2, 2, 64), ws=None, wsb=0) == -3  # decode workspace
     assert _forward(lib, mk=4) == -1                                   # sliding needs the window entry point
     st = S(2 * 16 * 64, 16 * 64, 64, 1)
     assert lib.sdpa_forward_sliding(4096, st, 4096, st, 4096, st, 1 << 20, st, 2, 16, 16, 16, 16, 64, 2, 0.125,

@@ -10,11 +10,13 @@ the call records a memset.  Each case below
      float64 oracle);
   2. captures one call into a graph, on a side stream, with an explicit
      workspace that eager calls share;
-  3. replays it several times; between replays the workspace is overwritten
-     with 0xff bytes (NaN patterns in float32) and an unrelated eager call of
-     another kernel family runs on the same workspace, with a synchronisation
-     before each replay.  Every replay must equal the eager result bit for bit
-     (the kernels are deterministic: fixed split order, no atomics);
+  3. replays it several times; between replays the workspace's partial
+     results are overwritten with 0xff bytes (NaN patterns in float32) and an
+     unrelated eager call of another kernel family runs on the same
+     workspace, with a synchronisation before each replay.  The workspace's
+     leading arrival words are left as the calls leave them (zero).  Every
+     replay must equal the eager result bit for bit (the kernels are
+     deterministic: fixed split order; the only atomics count arrivals);
   4. refills the captured inputs in place with new data and replays once
      more: the replay must equal an eager call on the new data.
 """
@@ -27,11 +29,17 @@ import sdpa_inputs as si
 
 pytestmark = pytest.mark.gpu
 
+COUNTER_BYTES = 32768  # leading arrival words of a decode workspace (zero before and after every call)
+
 # name, make_case arguments, route kind and a fragment of the route string
 CASES = [
-    ("decode-splits-combine", dict(B=1, Hq=32, Hkv=8, Lq=1, Lk=4096, D=256, mask_kind="additive"),
-     "vector", "splits=64"),
-    ("decode-one-split", dict(B=64, Hq=16, Hkv=8, Lq=1, Lk=256, D=128), "vector", "splits=1 "),
+    ("decode-fused-splits", dict(B=1, Hq=32, Hkv=8, Lq=1, Lk=4096, D=256, mask_kind="additive"),
+     "vector-fused", "splits=32"),
+    ("decode-fused-d512-vslices", dict(B=1, Hq=32, Hkv=4, Lq=1, Lk=4096, D=512, mask_kind="additive"),
+     "vector-fused", "vslices=2"),
+    ("decode-splits-combine", dict(B=1, Hq=12, Hkv=3, Lq=2, Lk=3000, D=128, mask_kind="additive"),
+     "vector ", "splits="),
+    ("decode-one-split", dict(B=64, Hq=16, Hkv=8, Lq=1, Lk=256, D=128), "vector-fused", "splits=1 "),
     ("decode-d512-causal-lq4", dict(B=2, Hq=8, Hkv=2, Lq=4, Lk=1000, D=512, mask_kind="causal"), "vector", ""),
     ("decode-qk192-v128", dict(B=1, Hq=16, Hkv=4, Lq=1, Lk=900, D=192, dv=128, mask_kind="additive"),
      "vector", ""),
@@ -85,7 +93,7 @@ def _check_graph(sdpa, call, refill_case, name):
     nbytes = sdpa.workspace_size(dims["batch"], dims["q_len"], dims["kv_len"], dims["n_q_heads"],
                                  dims["n_kv_heads"], dims["head_dim"], call.q.dtype,
                                  v_head_dim=call.v.shape[3])
-    ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device="cuda")
     eager = call(workspace=ws).clone()
     torch.cuda.synchronize()
 
@@ -104,7 +112,7 @@ def _check_graph(sdpa, call, refill_case, name):
     torch.cuda.synchronize()
 
     for rep in range(4):
-        ws.fill_(0xFF)
+        ws[COUNTER_BYTES:].fill_(0xFF)  # partial results need no initialisation; arrival words stay as left
         other(workspace=ws)
         call.out.fill_(float("nan"))
         torch.cuda.synchronize()

@@ -13,6 +13,10 @@ from gpu_util import DT_NAME, assert_parity, oracle_out, run_gpu, to_device
 pytestmark = pytest.mark.gpu
 
 HEAD_DIMS = [64, 72, 80, 96, 128, 256, 512]
+# leading arrival words of a decode workspace (zero before and after every call);
+# the last 128-byte line's first word counts groups recomputed by their last workgroup
+COUNTER_BYTES = 32768
+FALLBACK_WORD = (COUNTER_BYTES - 128) // 4
 DTYPES = ["f32", "f16", "bf16"]
 MASKS = ["none", "additive", "boolean", "causal"]
 
@@ -96,6 +100,60 @@ def test_decode_many_rows_per_group(gpu_lib, hq, hkv, lq):
     """n_rep * q_len beyond one 32-column block uses several column groups."""
     c = si.make_case(1, hq, hkv, lq, 257, 128, dtype="bf16", mask_kind="causal", seed=hq)
     assert_parity(run_gpu(c), oracle_out(c), "bf16", f"decode Hq={hq} Hkv={hkv} Lq={lq}")
+
+
+# Single-launch decode: groups of (batch, kv head, column group) that spread
+# evenly over the XCDs, every head dim, 16-bit type and mask kind, one row and
+# several per head (two column groups at q_len 8), a ragged key count.
+@pytest.mark.parametrize("lq", [1, 3, 8])
+@pytest.mark.parametrize("mask_kind", MASKS + ["sliding"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", HEAD_DIMS)
+def test_decode_fused_matrix(gpu_lib, D, dtype, mask_kind, lq):
+    c = si.make_case(2, 16, 4, lq, 1000, D, dtype=dtype, layout="bhld", mask_kind=mask_kind, seed=D + 7 * lq,
+                     mask_shape="full", mask_p=0.2, window=77 if mask_kind == "sliding" else None)
+    route = gpu_lib.describe_route(2, lq, 1000, 16, 4, D, c.q.dtype, mask_kind)
+    assert route.startswith("vector-fused"), route
+    assert_parity(run_gpu(c), oracle_out(c), dtype, f"decode fused D={D} {dtype} {mask_kind} Lq={lq}")
+
+
+@pytest.mark.parametrize("B,hq,hkv,lq,lk,D", [(1, 32, 8, 1, 4096, 256), (1, 32, 4, 1, 4096, 512),
+                                                (2, 16, 4, 5, 1000, 128), (4, 8, 2, 1, 333, 64)])
+def test_decode_fused_splits_share_one_xcd(gpu_lib, B, hq, hkv, lq, lk, D):
+    """Every group's splits ran on one XCD, so no last workgroup had to
+    recompute its group (the workspace's event word stays zero), and repeated
+    calls on one workspace give the same bits (its arrival words are left zero)."""
+    c = si.make_case(B, hq, hkv, lq, lk, D, dtype="bf16", layout="bhld", mask_kind="additive", seed=B + D)
+    q, k, v, m = to_device(c)
+    n = gpu_lib.workspace_size(B, lq, lk, hq, hkv, D, q.dtype)
+    ws = torch.zeros(max(n, COUNTER_BYTES), dtype=torch.uint8, device="cuda")
+    outs = [gpu_lib.forward(q, k, v, scale=c.scale, mask=m, mask_kind="additive", workspace=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    words = ws[:COUNTER_BYTES].view(torch.int32).cpu()
+    assert int(words[FALLBACK_WORD]) == 0, "a group's splits ran on several XCDs"
+    assert int(words[:FALLBACK_WORD].abs().sum()) == 0, "arrival words not reset"
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    assert_parity(outs[0], oracle_out(c), "bf16", f"decode fused B={B} Hq={hq} Hkv={hkv} D={D}")
+
+
+@pytest.mark.parametrize("mask_kind", ["additive", "causal"])
+def test_decode_fused_detects_splits_on_several_xcds(gpu_lib, monkeypatch, mask_kind):
+    """With a grid stride of 1 a group's splits are scattered over the XCDs:
+    the last workgroup of each group must notice (XCC-id sums) and recompute
+    the group itself, and the output must still match the oracle."""
+    monkeypatch.setenv("SDPA_FUSED_XCD_STRIDE", "1")
+    B, hq, hkv, lq, lk, D = 1, 32, 8, 2, 700, 128
+    c = si.make_case(B, hq, hkv, lq, lk, D, dtype="bf16", layout="bhld", mask_kind=mask_kind, seed=41,
+                     mask_shape="qk", mask_p=0.2)
+    q, k, v, m = to_device(c)
+    ws = torch.zeros(max(gpu_lib.workspace_size(B, lq, lk, hq, hkv, D, q.dtype), COUNTER_BYTES), dtype=torch.uint8,
+                     device="cuda")
+    out = gpu_lib.forward(q, k, v, scale=c.scale, mask=m, mask_kind=mask_kind, workspace=ws)
+    torch.cuda.synchronize()
+    words = ws[:COUNTER_BYTES].view(torch.int32).cpu()
+    assert int(words[FALLBACK_WORD]) == 8, f"groups recomputed: {int(words[FALLBACK_WORD])} (expected all 8)"
+    assert int(words[:FALLBACK_WORD].abs().sum()) == 0, "arrival words not reset"
+    assert_parity(out, oracle_out(c), "bf16", f"decode fused scattered splits {mask_kind}")
 
 
 # --------------------------------------------------------------------------
