@@ -5,11 +5,9 @@
 // merges them) is bound by reading K and V once from HBM.  Here the split and
 // the merge happen in one launch:
 //
-//   * A group is (batch, kv head, column group, V column slice): up to 16
-//     query rows (query heads of the kv head x query positions) that share
-//     every K/V byte, over the head-dim columns [vs * DOW, (vs + 1) * DOW) of V
-//     (VS = 1 or 2 slices; a slice re-reads K, never V).  Its keys are split
-//     over S workgroups.
+//   * A group is (batch, kv head, column group): up to 16 query rows (query
+//     heads of the kv head x query positions) that share every K/V byte.  Its
+//     keys are split over S workgroups.
 //   * Workgroup i of the 1-D grid serves group x + NX * ((i / NX) / S), split
 //     (i / NX) % S, x = i % NX, with NX the device's XCD count.  Workgroups are
 //     dispatched round-robin over the XCDs, so all S splits of a group run on
@@ -59,10 +57,10 @@ constexpr int kFusedCounterWords = kFusedCounterStride * kFusedCounterSlots;  //
 constexpr int kFusedFallbackWord = kFusedCounterStride * (kFusedCounterSlots - 1);  // groups recomputed by their last workgroup
 constexpr int kFusedMaxGroups = kFusedCounterSlots - 1;
 
-template <class TR, int D_, int DO_, int VS_, int NW_>
+template <class TR, int D_, int DO_, int NW_>
 struct DfCfg {
-    static constexpr int D = D_, DO = DO_, VS = VS_, NW = NW_, NT = 64 * NW;
-    static constexpr int DOW = DO / VS;                   // V / output columns per group
+    static constexpr int D = D_, DO = DO_, NW = NW_, NT = 64 * NW;
+    static constexpr int DOW = DO;                        // V / output columns of a group
     static constexpr int NCH = (D + 31) / 32;              // Q K^T steps of 32 head-dim columns
     static constexpr int DVP = (DOW + 15) / 16 * 16;       // V columns incl. pad to whole 16-column blocks
     static constexpr int NDB = DVP / 16;                   // O^T blocks (16 columns each)
@@ -78,7 +76,7 @@ struct DfCfg {
     static constexpr int LDS_G = 16 * 32 * 4 + 2 * 16 * (DOW / 4) * 16;  // group merge: weights, half sums
     static constexpr int LDS_W = LDS_V > LDS_M ? (LDS_V > LDS_G ? LDS_V : LDS_G) : (LDS_M > LDS_G ? LDS_M : LDS_G);
     static constexpr int LDS = LDS_W;
-    static_assert(DO % VS == 0 && DOW % 8 == 0, "V column slice must be whole 16-byte chunks");
+    static_assert(DOW % 8 == 0, "V rows must be whole 16-byte chunks");
     static_assert(D % 8 == 0, "head dim must be whole 16-byte chunks");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
@@ -119,41 +117,48 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
     __shared__ uint32_t s_word;
     char* const work = smem;
 
-    // Every kernel argument the prologue reads, fetched in one batch: left to
-    // itself the compiler issues these scalar loads next to their first uses,
-    // behind the branches and arithmetic of the prologue, and each batch is a
-    // round trip to kernel-argument memory (about a microsecond in all).
-    asm volatile("" ::"s"(fg.nx), "s"(fg.groups), "s"(fg.splits), "s"(fg.nblk), "s"(fg.rv), "s"(p.col_groups),
-                 "s"(p.Hkv), "s"(p.Lk), "s"(p.kbase), "s"(p.n_rep), "s"(p.Lq));
-    asm volatile("" ::"s"(p.k), "s"(p.v), "s"(p.q), "s"(p.ks[0]), "s"(p.ks[1]), "s"(p.ks[2]), "s"(p.vs[0]),
-                 "s"(p.vs[1]), "s"(p.vs[2]), "s"(p.qs[0]), "s"(p.qs[1]), "s"(p.qs[2]));
-    if constexpr (HAS_MT)
-        asm volatile("" ::"s"(p.mask), "s"(p.ms[0]), "s"(p.ms[1]), "s"(p.ms[2]), "s"(p.mask_span));
+    // Every 64-byte line of the argument block into the scalar cache in one
+    // batch (a load every 32 bytes reaches every line whatever the block's
+    // alignment).  Left to itself the compiler issues the argument loads in
+    // several batches, each waited for before the next, and every batch that
+    // misses the scalar cache is another round trip to memory before the first
+    // K/V load can go out.  The loads complete inside the asm statement.
+    static_assert(sizeof(Params) + sizeof(FusedGeom) <= 0x1a0, "argument block larger than the lines touched");
+    {
+        const __attribute__((address_space(4))) char* ka =
+            (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+        uint32_t t0, t1, t2, t3, t4, t5, t6, t7, t8, t9, t10, t11, t12;
+        asm volatile(
+            "s_load_dword %0, %13, 0x0\n s_load_dword %1, %13, 0x20\n s_load_dword %2, %13, 0x40\n"
+            "s_load_dword %3, %13, 0x60\n s_load_dword %4, %13, 0x80\n s_load_dword %5, %13, 0xa0\n"
+            "s_load_dword %6, %13, 0xc0\n s_load_dword %7, %13, 0xe0\n s_load_dword %8, %13, 0x100\n"
+            "s_load_dword %9, %13, 0x120\n s_load_dword %10, %13, 0x140\n s_load_dword %11, %13, 0x160\n"
+            "s_load_dword %12, %13, 0x180\n s_waitcnt lgkmcnt(0)"
+            : "=&s"(t0), "=&s"(t1), "=&s"(t2), "=&s"(t3), "=&s"(t4), "=&s"(t5), "=&s"(t6), "=&s"(t7), "=&s"(t8),
+              "=&s"(t9), "=&s"(t10), "=&s"(t11), "=&s"(t12)
+            : "s"(ka));
+        asm volatile("" ::"s"(t0 ^ t1 ^ t2 ^ t3 ^ t4 ^ t5 ^ t6 ^ t7 ^ t8 ^ t9 ^ t10 ^ t11 ^ t12));
+    }
 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g4 = lane >> 4;
 
     // ---- group and split of this workgroup (32-bit: the host keeps nblk * S below 2^31) ----
     const int i = blockIdx.x;
-    const int x = i % fg.nx, j = i / fg.nx;
-    const int grp = x + fg.nx * (j / fg.splits);
-    const int split = j % fg.splits;
-    // grp -> (b, kv head, column group, V slice); slice fastest
-    const int vs = grp % C::VS;
-    const int t = grp / C::VS;
-    const int cg = t % p.col_groups;
-    const int bk = t / p.col_groups;
-    const int kvh = bk % p.Hkv, b = bk / p.Hkv;
-    const int vcol0 = vs * DOW;
+    const int j = fast_div(i, fg.nx), x = i - j * fg.nx.d;
+    const int js = fast_div(j, fg.splits), split = j - js * fg.splits.d;
+    const int grp = x + fg.nx.d * js;
+    // grp -> (b, kv head, column group); column group fastest
+    const int bk = fast_div(grp, fg.colg), cg = grp - bk * fg.colg.d;
+    const int b = fast_div(bk, fg.hkv), kvh = bk - b * fg.hkv.d;
     // split s streams the 16-key blocks [s nblk / S, (s + 1) nblk / S); wave w takes
     // blocks blk0 + w + NW n
-    int blk0 = split * fg.nblk / fg.splits, blk1 = (split + 1) * fg.nblk / fg.splits;
+    int blk0 = fast_div(split * fg.nblk, fg.splits), blk1 = fast_div((split + 1) * fg.nblk, fg.splits);
 
     // ---- K / V: buffer resources over this (batch, kv head); rows past Lk read as zero ----
     const uint32_t kstep32 = (uint32_t)(p.ks[2] * 2), vstep32 = (uint32_t)(p.vs[2] * 2);
     const char* kglob = reinterpret_cast<const char*>(p.k) + ((int64_t)b * p.ks[0] + (int64_t)kvh * p.ks[1]) * 2;
-    const char* vglob = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)kvh * p.vs[1]) * 2 +
-                        (int64_t)vcol0 * 2;
+    const char* vglob = reinterpret_cast<const char*>(p.v) + ((int64_t)b * p.vs[0] + (int64_t)kvh * p.vs[1]) * 2;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kglob, (uint32_t)(p.Lk - 1) * kstep32 + (uint32_t)(D * 2));
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vglob, (uint32_t)(p.Lk - 1) * vstep32 + (uint32_t)(DOW * 2));
 
@@ -161,7 +166,7 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
     const int rows_g = min(16, p.n_rep * p.Lq - cg * 16);  // valid rows (<= fg.rv)
     const int r = col;
     const int rr = cg * 16 + (r < rows_g ? r : 0);
-    const int qh = kvh * p.n_rep + rr / p.Lq, qi = rr % p.Lq;
+    const int rq = fast_div(rr, fg.lq), qh = kvh * p.n_rep + rq, qi = rr - rq * fg.lq.d;
     const int off = p.Lk - p.Lq;
     // mask tensor (key-contiguous, 4-key aligned rows, below 4 GiB: checked on the host): one
     // range-checked vector load per 4 keys
@@ -171,14 +176,15 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
     uint32_t* const words = reinterpret_cast<uint32_t*>(p.ws_o);
     float* const part_o = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws_o) + kFusedCounterWords * 4);
     float* const part_ml = p.ws_ml;
-    const int S = fg.splits, RV = fg.rv;
+    const int S = fg.splits.d, RV = fg.rv;
     bool direct = S == 1;
     char* const vlds = work + w * (16 * C::PITCH * 16);
     // transposed-read offsets: lane (g4, e = (lane % 16) / 4, q = lane % 4) names row 4 g4 + e,
     // columns 16 db + 4 q .. + 3
     const uint32_t tr_off = (uint32_t)((4 * g4 + ((lane & 15) >> 2)) * C::PITCH * 16 + (lane & 3) * 8);
 
-    // Q fragments (B operand of S^T = K Q^T): row r, head-dim columns 32 c + 8 g4 .. +7.
+    // Q fragments (B operand of S^T = K Q^T): row r, head-dim columns 32 c + 8 g4 .. +7,
+    // zero for rows past the group (finite scores that are never stored; no load).
     // Loaded first: a wave's loads return in order, and S needs Q with the first K.
     u32x4_t qf[C::NCH];
     {
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
 #pragma unroll
         for (int c = 0; c < C::NCH; ++c) {
             const int d = 32 * c + 8 * g4;
-            qf[c] = d < D ? *reinterpret_cast<const u32x4_t*>(qrow + d * 2) : u32x4_t{0u, 0u, 0u, 0u};
+            qf[c] = (d < D && r < rows_g) ? *reinterpret_cast<const u32x4_t*>(qrow + d * 2) : u32x4_t{0u, 0u, 0u, 0u};
         }
         if constexpr (ROPE)
             rope_q_fragments<TR, C::NCH, 32>(qf, qrow, 8 * g4, p.rope_dim, p.rope_cos, p.rope_sin,
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
         for (int c = 0; c < C::NCH; ++c) {
             const int d = 32 * c + 8 * g4;
             kf[c] = u32x4_t{0u, 0u, 0u, 0u};
-            if (d < D) kf[c] = buffer_load16(krs, (uint32_t)(k0 + col) * kstep32 + (uint32_t)(d * 2));
+            if (d < D) kf[c] = buffer_load16_nt(krs, (uint32_t)(k0 + col) * kstep32 + (uint32_t)(d * 2));
         }
 #pragma unroll
         for (int u = 0; u < C::VU; ++u) {
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
             const int row = s / C::VCHP, ch = s % C::VCHP;
             vr[u] = u32x4_t{0u, 0u, 0u, 0u};
             if (s < C::VSLOTS && ch < C::VCH)
-                vr[u] = buffer_load16(vrs, (uint32_t)(k0 + row) * vstep32 + (uint32_t)(ch * 16));
+                vr[u] = buffer_load16_nt(vrs, (uint32_t)(k0 + row) * vstep32 + (uint32_t)(ch * 16));
         }
         if constexpr (HAS_MT) mr = load_mask_group_rs<MASK>(mrs, (mrow + (uint32_t)(k0 + 4 * g4)) * MES);
     };
@@ -328,10 +334,10 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
             if (direct) {
                 if (row < rows_g) {
                     const int rg = cg * 16 + row;
-                    const int oqh = kvh * p.n_rep + rg / p.Lq, oqi = rg % p.Lq;
+                    const int rgq = fast_div(rg, fg.lq), oqh = kvh * p.n_rep + rgq, oqi = rg - rgq * fg.lq.d;
                     const float inv = l > 0.f ? 1.f / l : 0.f;
                     char* dst = reinterpret_cast<char*>(p.o) +
-                                ((int64_t)b * p.os[0] + (int64_t)oqh * p.os[1] + (int64_t)oqi * p.os[2] + vcol0 + c4) * 2;
+                                ((int64_t)b * p.os[0] + (int64_t)oqh * p.os[1] + (int64_t)oqi * p.os[2] + c4) * 2;
                     TR::store4(dst, o * inv);
                 }
             } else {
@@ -439,9 +445,9 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
             f32x4_t o = ob[it];
             for (int h = 1; h < halves; ++h) o += ob[h * nitems + it];
             const int rg = cg * 16 + row;
-            const int oqh = kvh * p.n_rep + rg / p.Lq, oqi = rg % p.Lq;
+            const int rgq = fast_div(rg, fg.lq), oqh = kvh * p.n_rep + rgq, oqi = rg - rgq * fg.lq.d;
             char* dst = reinterpret_cast<char*>(p.o) +
-                        ((int64_t)b * p.os[0] + (int64_t)oqh * p.os[1] + (int64_t)oqi * p.os[2] + vcol0 + c4) * 2;
+                        ((int64_t)b * p.os[0] + (int64_t)oqh * p.os[1] + (int64_t)oqi * p.os[2] + c4) * 2;
             TR::store4(dst, o);
         }
         return;

@@ -45,9 +45,9 @@ struct KernelSet {
     // 16-bit decode in one launch (split keys merged in L2 by the last
     // workgroup of each group), by V column slices (index VS - 1; null where
     // not built) and mask variant
-    fused_fn decode_fused[2][sdpa_dev::MASK_VARIANTS];
-    fused_fn decode_fused_rope[2][sdpa_dev::MASK_VARIANTS];
-    int fused_nt[2];  // threads per workgroup of those kernels, by V slices
+    fused_fn decode_fused[sdpa_dev::MASK_VARIANTS];
+    fused_fn decode_fused_rope[sdpa_dev::MASK_VARIANTS];
+    int fused_nt;  // threads per workgroup of those kernels (0: none built)
 };
 
 // Returns hipErrorInvalidConfiguration when the compiled kernel cannot run

@@ -202,13 +202,11 @@ size_t decode_ws_bytes(int batch, int q_len, int hq, int d, long splits, sdpa_dt
     return kCounterBytes + align256(rows * splits * d * sizeof(float)) + align256(rows * splits * 2 * sizeof(float));
 }
 
-// Single-launch decode (16-bit): groups of (batch, kv head, column group of
-// <= 16 rows, V column slice) whose splits all run on one XCD.  Taken when the
-// groups spread evenly over the XCDs (with two V slices if that is what it
-// takes); otherwise the split + combine kernels run.
+// Single-launch decode (16-bit, D <= 256): groups of (batch, kv head, column
+// group of <= 16 rows) whose splits all run on one XCD.  Taken when the groups
+// spread evenly over the XCDs; otherwise the split + combine kernels run.
 struct FusedPlan {
     bool use = false;
-    int vs = 1;       // V column slices
     int groups = 0;   // G
     int splits = 1;   // S
     int nblk = 0;     // 16-key blocks from kbase
@@ -217,26 +215,21 @@ struct FusedPlan {
 };
 constexpr int kFusedKeys = 16;  // keys per block of the single-launch kernel
 
-FusedPlan fused_plan(const KernelSet* ks, int batch, int q_len, int kv_len_eff, int hq, int hkv, int dv, int rope,
+FusedPlan fused_plan(const KernelSet* ks, int batch, int q_len, int kv_len_eff, int hq, int hkv, int rope,
                      int variant, bool mask_ok = true) {
     FusedPlan f;
-    if (!ks || !ks->fused_nt[0] || !mask_ok) return f;
+    if (!ks || !ks->fused_nt || !mask_ok) return f;
+    // SDPA_DECODE_FUSED=0: the split + combine kernels for every decode shape (comparisons, tests)
+    if (const char* env = std::getenv("SDPA_DECODE_FUSED"))
+        if (env[0] == '0') return f;
+    if ((rope ? ks->decode_fused_rope[variant] : ks->decode_fused[variant]) == nullptr) return f;
     const DevInfo di = device_info();
     const int nx = di.nx;
     const int rows = (hq / hkv) * q_len;
     f.col_groups = (rows + 15) / 16;
     f.rv = rows < 16 ? rows : 16;
-    const long g1 = (long)batch * hkv * f.col_groups;
-    auto built = [&](int vs) {
-        return (rope ? ks->decode_fused_rope[vs - 1][variant] : ks->decode_fused[vs - 1][variant]) != nullptr;
-    };
-    int vs = 0;
-    if (g1 % nx == 0 && built(1)) vs = 1;
-    else if ((2 * g1) % nx == 0 && built(2) && dv % 32 == 0) vs = 2;
-    if (!vs) return f;
-    const long G = g1 * vs;
-    if (G > (1L << 30)) return f;
-    f.vs = vs;
+    const long G = (long)batch * hkv * f.col_groups;
+    if (G % nx != 0 || G > (1L << 30)) return FusedPlan{};
     f.groups = (int)G;
     f.nblk = (kv_len_eff + kFusedKeys - 1) / kFusedKeys;
     // one workgroup per CU: S splits per group
@@ -261,7 +254,7 @@ FusedPlan fused_plan(const KernelSet* ks, int batch, int q_len, int kv_len_eff, 
 size_t fused_ws_bytes(const FusedPlan& f, int dv) {
     if (f.splits == 1) return 0;
     const size_t slots = (size_t)f.groups * f.splits * f.rv;
-    return kCounterBytes + align256(slots * (dv / f.vs) * sizeof(float)) + align256(slots * 2 * sizeof(float));
+    return kCounterBytes + align256(slots * dv * sizeof(float)) + align256(slots * 2 * sizeof(float));
 }
 
 // Byte extent of a strided tensor: [base, base + span).
@@ -386,13 +379,13 @@ std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int 
                       t.lds, fg.items, fg.pairs ? " causal-pairs" : "");
     } else {
         const auto& t = ks->dec_cfg;
-        const FusedPlan f = fused_plan(ks, batch, q_len, kv_len, hq, hkv, dv, 0, kernel_variant(mk, SDPA_BF16));
+        const FusedPlan f = fused_plan(ks, batch, q_len, kv_len, hq, hkv, 0, kernel_variant(mk, SDPA_BF16));
         if (f.use) {
             std::snprintf(buf, sizeof buf,
-                          "vector-fused %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d groups=%d vslices=%d splits=%d "
+                          "vector-fused %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d groups=%d splits=%d "
                           "blocks/split=%d colgroups=%d threads=%d xcds=%d",
-                          dtype_name(dt), dn, mask_name(mk), batch, q_len, kv_len, hq, hkv, f.groups, f.vs, f.splits,
-                          (f.nblk + f.splits - 1) / f.splits, f.col_groups, ks->fused_nt[f.vs - 1],
+                          dtype_name(dt), dn, mask_name(mk), batch, q_len, kv_len, hq, hkv, f.groups, f.splits,
+                          (f.nblk + f.splits - 1) / f.splits, f.col_groups, ks->fused_nt,
                           device_info().nx);
         } else {
             DecodePlan p = decode_plan(batch, q_len, kv_len, hq, hkv, t);
@@ -492,7 +485,7 @@ size_t sdpa_workspace_size_ex(int batch, int q_len, int kv_len, int n_q_heads, i
     for (int rope = 0; rope < 2; ++rope)
         for (int var = 0; var < sdpa_dev::MASK_VARIANTS; ++var) {
             // (a mask tensor without aligned 4-key runs takes the split + combine kernels)
-            const FusedPlan f = fused_plan(ks, batch, q_len, kv_len, n_q_heads, n_kv_heads, v_head_dim, rope, var);
+            const FusedPlan f = fused_plan(ks, batch, q_len, kv_len, n_q_heads, n_kv_heads, rope, var);
             const size_t bf = f.use ? fused_ws_bytes(f, v_head_dim) : 0;
             const size_t bs = decode_ws_bytes(batch, q_len, n_q_heads, v_head_dim,
                                               split_cap(batch, q_len, kv_len, n_q_heads, n_kv_heads, ks->dec_cfg,
@@ -722,8 +715,8 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     }
     // the single-launch kernel reads mask tensors in aligned 4-key vectors with 32-bit offsets
     const bool mask_ok = !p.mask || (p.mask_vec && p.mask_span < (int64_t)0xffffffffLL);
-    const FusedPlan fpl = fused_plan(ks, batch, q_len, kv_len - p.kbase, n_q_heads, n_kv_heads, v_head_dim,
-                                     p.rope_dim > 0, mk, mask_ok);
+    const FusedPlan fpl = fused_plan(ks, batch, q_len, kv_len - p.kbase, n_q_heads, n_kv_heads, p.rope_dim > 0,
+                                     mk, mask_ok);
     if (fpl.use) {
         const size_t need = fused_ws_bytes(fpl, v_head_dim);
         if (need && (!workspace || workspace_bytes < need)) return reject(SDPA_EWORKSPACE);
@@ -735,20 +728,21 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         const size_t slots = (size_t)fpl.groups * fpl.splits * fpl.rv;
         p.ws_o = reinterpret_cast<float*>(workspace);
         p.ws_ml = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kCounterBytes +
-                                                  align256(slots * (v_head_dim / fpl.vs) * sizeof(float)))
+                                                  align256(slots * v_head_dim * sizeof(float)))
                        : nullptr;
         p.col_groups = fpl.col_groups;
-        sdpa_dev::FusedGeom fg{di.nx, fpl.groups, fpl.splits, fpl.nblk, fpl.rv};
+        sdpa_dev::FusedGeom fg{sdpa_dev::make_fastdiv(di.nx), sdpa_dev::make_fastdiv(fpl.splits),
+                               sdpa_dev::make_fastdiv(fpl.col_groups), sdpa_dev::make_fastdiv(n_kv_heads),
+                               sdpa_dev::make_fastdiv(q_len), fpl.groups, fpl.nblk, fpl.rv};
         // test-only: another XCD stride scatters a group's splits over several XCDs,
         // which the kernel must detect (and recompute the group)
         if (const char* env = std::getenv("SDPA_FUSED_XCD_STRIDE")) {
             const long v = std::strtol(env, nullptr, 10);
-            if (v > 0 && fpl.groups % v == 0) fg.nx = (int)v;
+            if (v > 0 && fpl.groups % v == 0) fg.nx = sdpa_dev::make_fastdiv((int)v);
         }
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
                                     mask_kind, st, kern, reason));
-        const sdpa_host::fused_fn f = p.rope_dim > 0 ? ks->decode_fused_rope[fpl.vs - 1][mk]
-                                                     : ks->decode_fused[fpl.vs - 1][mk];
+        const sdpa_host::fused_fn f = p.rope_dim > 0 ? ks->decode_fused_rope[mk] : ks->decode_fused[mk];
         if (!f) return reject(SDPA_EUNSUPPORTED);
         mark(0);
         st = hip_status(f(p, fg, dim3((unsigned)(fpl.groups * fpl.splits)), s));

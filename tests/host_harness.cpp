@@ -7,7 +7,9 @@
 // addresses.
 #include "sdpa_host.cpp"
 
+#include <random>
 #include <thread>
+#include <vector>
 
 #include "decode_kernel.h"
 
@@ -64,16 +66,14 @@ sdpa_host::KernelSet make_set() {
         k.decode[m] = stub;
         if (TR::ES == 2) {
             k.decode_rope[m] = stub;
-            k.decode_fused[0][m] = stub_fused;
-            k.decode_fused_rope[0][m] = stub_fused;
-            if (D >= 256 && DV == D) {
-                k.decode_fused[1][m] = stub_fused;
-                k.decode_fused_rope[1][m] = stub_fused;
+            if (D <= 256) {  // as the instantiation units: the single-launch kernel up to D = 256
+                k.decode_fused[m] = stub_fused;
+                k.decode_fused_rope[m] = stub_fused;
             }
         }
     }
     k.combine = stub;
-    if (TR::ES == 2) k.fused_nt[0] = k.fused_nt[1] = 512;
+    if (TR::ES == 2 && D <= 256) k.fused_nt = 512;
     // tile shapes as the instantiation units declare them (the planner reads bn, cols, nt)
     if constexpr (TR::ES == 2) {
         using V = sdpa_dev::DecCfg<TR, D, 4, DV>;
@@ -113,8 +113,8 @@ sdpa_strides bhld(int H, int L, int D) { return sdpa_strides{(int64_t)H * L * D,
 size_t touched(const Launch& l, int dv) {
     const char* base = (const char*)kW;
     if (l.fused) {
-        if (l.fg.splits == 1) return 0;
-        const size_t slots = (size_t)l.fg.groups * l.fg.splits * l.fg.rv;
+        if (l.fg.splits.d == 1) return 0;
+        const size_t slots = (size_t)l.fg.groups * l.fg.splits.d * l.fg.rv;
         const size_t o_end = (size_t)((const char*)l.p.ws_o - base) + 32768 + slots * (dv / (l.fg.groups / (l.p.B * l.p.Hkv * l.p.col_groups))) * 4;
         const size_t ml_beg = (size_t)((const char*)l.p.ws_ml - base);
         if (o_end > ml_beg) return (size_t)-1;
@@ -181,15 +181,15 @@ void check_fused_geometry() {
     g_last = Launch{};
     const size_t ws = sdpa_workspace_size(1, 1, 4096, 32, 8, 256, SDPA_BF16);
     CHECK(call(1, 1, 4096, 32, 8, 256, 256, SDPA_BF16, SDPA_MASK_ADDITIVE, 0, ws) == SDPA_OK, "c2");
-    CHECK(g_last.fused && g_last.fg.groups == 8 && g_last.fg.splits == 32 && g_last.grid == 256 &&
+    CHECK(g_last.fused && g_last.fg.groups == 8 && g_last.fg.splits.d == 32 && g_last.grid == 256 &&
               g_last.fg.nblk == 256 && g_last.fg.rv == 4,
-          "c2 geometry fused=%d G=%d S=%d grid=%u", (int)g_last.fused, g_last.fg.groups, g_last.fg.splits,
+          "c2 geometry fused=%d G=%d S=%d grid=%u", (int)g_last.fused, g_last.fg.groups, g_last.fg.splits.d,
           g_last.grid);
     g_last = Launch{};
     const size_t ws3 = sdpa_workspace_size(1, 1, 4096, 32, 4, 512, SDPA_BF16);
     CHECK(call(1, 1, 4096, 32, 4, 512, 512, SDPA_BF16, SDPA_MASK_ADDITIVE, 0, ws3) == SDPA_OK, "c3");
-    CHECK(g_last.fused && g_last.fg.groups == 8 && g_last.fg.splits == 32 && g_last.p.col_groups == 1,
-          "c3 geometry G=%d S=%d", g_last.fg.groups, g_last.fg.splits);
+    CHECK(!g_last.fused && g_last.calls == 2, "c3 (D = 512): split + combine, fused=%d launches=%d",
+          (int)g_last.fused, g_last.calls);
     // groups that do not spread evenly over the XCDs: split + combine kernels
     g_last = Launch{};
     const size_t ws4 = sdpa_workspace_size(1, 2, 3000, 12, 3, 128, SDPA_BF16);
@@ -199,7 +199,82 @@ void check_fused_geometry() {
     CHECK(sdpa_workspace_size(64, 1, 512, 16, 8, 128, SDPA_BF16) == 0, "batch 64 needs no workspace");
     g_last = Launch{};
     CHECK(call(64, 1, 512, 16, 8, 128, 128, SDPA_BF16, SDPA_MASK_NONE, 0, 0, 0) == SDPA_OK, "batch 64");
-    CHECK(g_last.fused && g_last.fg.splits == 1, "batch 64: S=%d", g_last.fg.splits);
+    CHECK(g_last.fused && g_last.fg.splits.d == 1, "batch 64: S=%d", g_last.fg.splits.d);
+}
+
+// fast_div against the hardware division: divisors at and around every power
+// of two and random ones, numerators at the edges of each quotient step and
+// random ones below 2^31
+void check_fast_div() {
+    std::mt19937_64 rng(7);
+    std::vector<int> ds;
+    for (int l = 0; l < 31; ++l)
+        for (int e = -2; e <= 2; ++e) {
+            const long long d = (1LL << l) + e;
+            if (d >= 1 && d < (1LL << 31)) ds.push_back((int)d);
+        }
+    for (int r = 0; r < 2000; ++r) ds.push_back(1 + (int)(rng() % ((1ULL << 31) - 1)));
+    for (int r = 0; r < 2000; ++r) ds.push_back(1 + (int)(rng() % 300));
+    for (const int d : ds) {
+        const sdpa_dev::FastDiv f = sdpa_dev::make_fastdiv(d);
+        std::vector<long long> ns = {0, 1, d - 1LL, d, d + 1LL, (1LL << 31) - 1, (1LL << 31) - 2, (1LL << 31) - d};
+        const long long qmax = ((1LL << 31) - 1) / d;
+        for (int r = 0; r < 64; ++r) {
+            const long long q = (long long)(rng() % (unsigned long long)(qmax + 1));
+            ns.push_back(q * d);
+            ns.push_back(q * d - 1);
+            ns.push_back(q * d + d - 1);
+            ns.push_back((long long)(rng() % (1ULL << 31)));
+        }
+        for (const long long n : ns) {
+            if (n < 0 || n >= (1LL << 31)) continue;
+            CHECK(sdpa_dev::fast_div((int)n, f) == (int)(n / d), "fast_div(%lld, %d) = %d", n, d,
+                  sdpa_dev::fast_div((int)n, f));
+        }
+    }
+}
+
+// The single-launch decode kernel's workgroup -> (group, split) mapping, taken
+// on the host with the geometry the planner launched: every (group, split)
+// exactly once, the splits of a group on one XCD (workgroup i on XCD i % nx),
+// and the split key ranges tile [0, nblk) in order.
+void check_fused_mapping() {
+    struct Shape { int b, lq, lk, hq, hkv, d; };
+    const Shape shapes[] = {{1, 1, 4096, 32, 8, 256}, {1, 1, 4096, 32, 4, 512}, {2, 3, 1000, 16, 4, 128},
+                            {1, 8, 5000, 64, 8, 64},   {4, 1, 333, 8, 2, 96},    {1, 2, 70000, 16, 16, 128}};
+    for (const Shape& sh : shapes) {
+        g_last = Launch{};
+        const size_t ws = sdpa_workspace_size(sh.b, sh.lq, sh.lk, sh.hq, sh.hkv, sh.d, SDPA_BF16);
+        CHECK(call(sh.b, sh.lq, sh.lk, sh.hq, sh.hkv, sh.d, sh.d, SDPA_BF16, SDPA_MASK_NONE, 0, ws) == SDPA_OK,
+              "mapping shape Hq=%d Hkv=%d", sh.hq, sh.hkv);
+        if (!g_last.fused) continue;
+        const sdpa_dev::FusedGeom& fg = g_last.fg;
+        const int S = fg.splits.d, G = fg.groups, nx = fg.nx.d;
+        CHECK((long)G * S == (long)g_last.grid, "grid %u for G=%d S=%d", g_last.grid, G, S);
+        CHECK(fg.colg.d == g_last.p.col_groups && fg.hkv.d == sh.hkv && fg.lq.d == sh.lq, "divisors");
+        std::vector<int> seen((size_t)G * S, 0), xcd(G, -1);
+        std::vector<int> lo((size_t)G * S), hi((size_t)G * S);
+        for (int i = 0; i < (int)g_last.grid; ++i) {
+            const int j = sdpa_dev::fast_div(i, fg.nx), x = i - j * nx;
+            const int js = sdpa_dev::fast_div(j, fg.splits), split = j - js * S;
+            const int grp = x + nx * js;
+            CHECK(grp >= 0 && grp < G && split >= 0 && split < S, "workgroup %d -> group %d split %d", i, grp,
+                  split);
+            if (grp < 0 || grp >= G) continue;
+            ++seen[(size_t)grp * S + split];
+            if (xcd[grp] < 0) xcd[grp] = i % nx;
+            CHECK(xcd[grp] == i % nx, "group %d on XCDs %d and %d", grp, xcd[grp], i % nx);
+            lo[(size_t)grp * S + split] = sdpa_dev::fast_div(split * fg.nblk, fg.splits);
+            hi[(size_t)grp * S + split] = sdpa_dev::fast_div((split + 1) * fg.nblk, fg.splits);
+        }
+        for (int g = 0; g < G; ++g)
+            for (int s2 = 0; s2 < S; ++s2) {
+                const size_t k = (size_t)g * S + s2;
+                CHECK(seen[k] == 1, "group %d split %d seen %d times", g, s2, seen[k]);
+                CHECK(lo[k] == (s2 ? hi[k - 1] : 0) && lo[k] < hi[k], "split %d keys [%d, %d)", s2, lo[k], hi[k]);
+            }
+        CHECK(hi[(size_t)S - 1] == fg.nblk, "last split ends at %d of %d", hi[(size_t)S - 1], fg.nblk);
+    }
 }
 
 void check_overlaps() {
@@ -239,6 +314,8 @@ void concurrent_queries() {
 int main() {
     sweep_workspace_bound();
     check_fused_geometry();
+    check_fast_div();
+    check_fused_mapping();
     check_overlaps();
     concurrent_queries();
     std::printf("host harness: %ld checks, %d failed\n", g_checks, g_fail);

@@ -85,11 +85,13 @@ def test_value_head_dim_pairing(lib):
 
 
 def test_describe_route(lib):
-    # 4 kv heads over 8 XCDs: two V column slices make 8 groups, one launch
+    # head dim 512: split + combine kernels (the single-launch kernel stops at 256)
     s = sdpa.describe_route(1, 1, 4096, 32, 4, 512, 2, "additive")
-    assert s.startswith("vector-fused bf16 d512 additive") and "vslices=2" in s and "splits=32" in s, s
+    assert s.startswith("vector bf16 d512 additive") and "splits=" in s, s
     s = sdpa.describe_route(1, 1, 4096, 32, 8, 256, 2, "additive")
-    assert s.startswith("vector-fused bf16 d256 additive") and "groups=8 vslices=1 splits=32" in s, s
+    assert s.startswith("vector-fused bf16 d256 additive") and "groups=8 splits=32" in s, s
+    # 4 kv heads cannot spread over 8 XCDs: split + combine
+    assert sdpa.describe_route(1, 1, 4096, 32, 4, 256, 2, "additive").startswith("vector bf16")
     # 3 kv heads do not spread evenly over the XCDs: split + combine kernels
     s = sdpa.describe_route(1, 1, 4096, 12, 3, 128, 2, "none")
     assert s.startswith("vector bf16 d128 none") and "splits=" in s, s
@@ -106,12 +108,12 @@ def test_workspace_size(lib):
     # single-launch decode: 32 KiB of arrival words, then per (group, split, row) one
     # fp32 partial row of the group's V columns and its (max, sum)
     # (a mask tensor without aligned 4-key runs takes the split + combine kernels: the size covers both)
-    ws = sdpa.workspace_size(1, 1, 4096, 32, 4, 512, 2)
-    route = sdpa.describe_route(1, 1, 4096, 32, 4, 512, 2)
-    G, vs, S = (int(re.search(k + r"=(\d+)", route).group(1)) for k in ("groups", "vslices", "splits"))
-    slots = G * S * 8                                                   # 8 query heads per kv head, q_len 1
-    fused = 32768 + align(slots * (512 // vs) * 4) + align(slots * 2 * 4)
-    split_combine = 32768 + align(32 * 64 * 512 * 4) + align(32 * 64 * 2 * 4)
+    ws = sdpa.workspace_size(1, 1, 4096, 32, 8, 256, 2)
+    route = sdpa.describe_route(1, 1, 4096, 32, 8, 256, 2)
+    G, S = (int(re.search(k + r"=(\d+)", route).group(1)) for k in ("groups", "splits"))
+    slots = G * S * 4                                                   # 4 query heads per kv head, q_len 1
+    fused = 32768 + align(slots * 256 * 4) + align(slots * 2 * 4)
+    split_combine = 32768 + align(32 * 64 * 256 * 4) + align(32 * 64 * 2 * 4)
     assert ws == max(fused, split_combine)
     # split + combine: per (query row, split) one fp32 output row and (max, sum); the
     # split count is the largest any key count up to kv_len plans

@@ -35,8 +35,8 @@ COUNTER_BYTES = 32768  # leading arrival words of a decode workspace (zero befor
 CASES = [
     ("decode-fused-splits", dict(B=1, Hq=32, Hkv=8, Lq=1, Lk=4096, D=256, mask_kind="additive"),
      "vector-fused", "splits=32"),
-    ("decode-fused-d512-vslices", dict(B=1, Hq=32, Hkv=4, Lq=1, Lk=4096, D=512, mask_kind="additive"),
-     "vector-fused", "vslices=2"),
+    ("decode-d512-splits-combine", dict(B=1, Hq=32, Hkv=4, Lq=1, Lk=4096, D=512, mask_kind="additive"),
+     "vector ", "splits="),
     ("decode-splits-combine", dict(B=1, Hq=12, Hkv=3, Lq=2, Lk=3000, D=128, mask_kind="additive"),
      "vector ", "splits="),
     ("decode-one-split", dict(B=64, Hq=16, Hkv=8, Lq=1, Lk=256, D=128), "vector-fused", "splits=1 "),
