@@ -222,6 +222,36 @@ int sdpa_forward_ex(const void* q, sdpa_strides q_st,
                     void* stream);
 
 /*
+ * sdpa_forward_noalloc -- sdpa_forward_ex for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): no workspace argument; the vector kernel keeps its
+ * per-split partial results and arrival counters in a static device array of
+ * sdpa_noalloc_scratch_bytes() bytes (8 MiB) that every GPU the library runs
+ * on holds until the process ends.  The call allocates and frees nothing; the
+ * first call on a device looks up that device's copy of the array.  A shape
+ * whose sdpa_workspace_size_ex() exceeds the array returns SDPA_EWORKSPACE
+ * (use sdpa_forward_ex with a workspace).  The arrival counters are zero when
+ * the library is loaded and every completed call leaves them zero.  All calls
+ * on one GPU share the array: calls that may overlap on one GPU (different
+ * streams, or host threads without ordering) race and give wrong results.
+ * Every other argument, status and rule as sdpa_forward_ex.
+ */
+int sdpa_forward_noalloc(const void* q, sdpa_strides q_st,
+                         const void* k, sdpa_strides k_st,
+                         const void* v, sdpa_strides v_st,
+                         void* out, sdpa_strides o_st,
+                         int batch, int q_len, int kv_len,
+                         int n_q_heads, int n_kv_heads, int head_dim, int v_head_dim,
+                         sdpa_dtype dtype, float scale,
+                         sdpa_mask_kind mask_kind, const void* mask, sdpa_strides mask_st,
+                         sdpa_dtype mask_dtype, int window,
+                         const sdpa_rope_table* q_rope, int q_pos0,
+                         void* stream);
+
+/* sdpa_noalloc_scratch_bytes -- size of the static scratch of sdpa_forward_noalloc. */
+size_t sdpa_noalloc_scratch_bytes(void);
+
+/*
  * sdpa_rope -- y = the rotary embedding of x (see sdpa_rope_table): row l of
  * every (batch, head) sits at position pos0 + l.  x and y are device
  * [batch, n_heads, len, head_dim] tensors of `dtype` (F32, F16, BF16) with

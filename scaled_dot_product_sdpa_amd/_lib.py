@@ -29,7 +29,8 @@ EXPORTS = ("sdpa_forward", "sdpa_forward_sliding", "sdpa_forward_ex", "sdpa_rope
            "sdpa_select_kernel_ex", "sdpa_describe_route", "sdpa_describe_route_ex", "sdpa_workspace_size",
            "sdpa_workspace_size_ex",
            "sdpa_head_dims", "sdpa_strerror", "sdpa_last_hip_error", "sdpa_route_counters",
-           "sdpa_timing_start", "sdpa_timing_stop", "sdpa_probe_stream_read")
+           "sdpa_timing_start", "sdpa_timing_stop", "sdpa_probe_stream_read", "sdpa_forward_noalloc",
+           "sdpa_noalloc_scratch_bytes")
 
 
 class Strides(ctypes.Structure):
@@ -100,6 +101,12 @@ def load(path: str = LIB_PATH):
         lib.sdpa_timing_stop.restype = i
         lib.sdpa_probe_stream_read.argtypes = [vp, sz, vp, vp]
         lib.sdpa_probe_stream_read.restype = i
+        lib.sdpa_forward_noalloc.argtypes = [vp, Strides, vp, Strides, vp, Strides, vp, Strides,
+                                             i, i, i, i, i, i, i, i, ctypes.c_float, i, vp, Strides, i, i,
+                                             ctypes.POINTER(RopeTable), i, vp]
+        lib.sdpa_forward_noalloc.restype = i
+        lib.sdpa_noalloc_scratch_bytes.argtypes = []
+        lib.sdpa_noalloc_scratch_bytes.restype = sz
         _lib = lib
         return lib
 
@@ -231,7 +238,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
             mask: Optional[torch.Tensor] = None, mask_kind: Optional[str] = None,
             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
             layout: str = "bhld", window: Optional[int] = None, rope=None,
-            q_pos0: Optional[int] = None) -> torch.Tensor:
+            q_pos0: Optional[int] = None, no_alloc: bool = False) -> torch.Tensor:
     """softmax(scale * q k^T + mask) v on the GPU through libsdpa.so.
 
     q: [B, Hq, Lq, D], k: [B, Hkv, Lk, D], v: [B, Hkv, Lk, Dv] in logical order (any strides,
@@ -243,6 +250,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
     rope: (cos, sin, rotary_dim) rotates Q inside the kernels (K must already
     be rotated, e.g. by rope() below); query row i sits at position
     q_pos0 + i, q_pos0 defaulting to Lk - Lq.
+    no_alloc: call sdpa_forward_noalloc (the library's static scratch instead of
+    a workspace; pass `out` as well for a call that allocates nothing at all).
     """
     lib = load()
     if layout == "blhd":
@@ -280,6 +289,18 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
         mptr, mst, mdt = mask.data_ptr(), _strides(mask), dtype_code(mask.dtype)
     if out is None:
         out = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
+    if no_alloc:
+        table = _rope_table(*rope, device=q.device) if rope is not None else None
+        if q_pos0 is None:
+            q_pos0 = Lk - Lq
+        st = lib.sdpa_forward_noalloc(q.data_ptr(), _strides(q), k.data_ptr(), _strides(k), v.data_ptr(),
+                                      _strides(v), out.data_ptr(), _strides(out), B, Lq, Lk, Hq, Hkv, D, Dv, dt,
+                                      float(scale), mk, mptr, mst, mdt, int(window or 0),
+                                      ctypes.byref(table) if table is not None else None, int(q_pos0),
+                                      torch.cuda.current_stream(q.device).cuda_stream)
+        if st != 0:
+            raise SdpaError(st, f"sdpa_forward_noalloc(B={B}, Lq={Lq}, Lk={Lk}, Hq={Hq}, Hkv={Hkv}, D={D})")
+        return out.transpose(1, 2) if layout == "blhd" else out
     nbytes = lib.sdpa_workspace_size_ex(B, Lq, Lk, Hq, Hkv, D, Dv, dt)
     if workspace is None:
         workspace = _workspace(nbytes, q.device)

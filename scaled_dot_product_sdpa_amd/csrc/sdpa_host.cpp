@@ -570,7 +570,35 @@ int sdpa_route_counters(uint64_t* out, int n) {
 
 }  // extern "C"
 
+// The allocation-free entry point's scratch: one static device array per GPU
+// (the code object is loaded on every device the library runs on), zero at
+// load.  Host code never passes the array's name to a kernel: it keeps the
+// device address hipGetSymbolAddress returns for each device, taken once with
+// that device current.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_pointer(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return SDPA_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!ptr || ((uintptr_t)ptr) % 256 != 0) return SDPA_EHIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SDPA_OK;
+}
 
 int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
                  sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len, int n_q_heads,
@@ -828,6 +856,29 @@ int sdpa_forward_ex(const void* q, sdpa_strides q_st, const void* k, sdpa_stride
                         mask_kind == SDPA_MASK_SLIDING ? window : 0, q_rope, q_pos0, workspace, workspace_bytes,
                         stream);
 }
+
+int sdpa_forward_noalloc(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
+                         sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len,
+                         int n_q_heads, int n_kv_heads, int head_dim, int v_head_dim, sdpa_dtype dtype, float scale,
+                         sdpa_mask_kind mask_kind, const void* mask, sdpa_strides mask_st, sdpa_dtype mask_dtype,
+                         int window, const sdpa_rope_table* q_rope, int q_pos0, void* stream) {
+    g_counters[0].fetch_add(1, std::memory_order_relaxed);
+    if (mask_kind == SDPA_MASK_SLIDING && window < 1) return reject(SDPA_EINVAL);
+    const size_t need = sdpa_workspace_size_ex(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim,
+                                               dtype);
+    if (need > kScratchBytes) return reject(SDPA_EWORKSPACE);
+    void* ws = nullptr;
+    if (need) {
+        const int st = scratch_pointer(&ws);
+        if (st != SDPA_OK) return reject(st);
+    }
+    return forward_impl(q, q_st, k, k_st, v, v_st, out, o_st, batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim,
+                        v_head_dim, dtype, scale, mask_kind, mask, mask_st, mask_dtype,
+                        mask_kind == SDPA_MASK_SLIDING ? window : 0, q_rope, q_pos0, ws, need ? kScratchBytes : 0,
+                        stream);
+}
+
+size_t sdpa_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int sdpa_rope(const void* x, sdpa_strides x_st, void* y, sdpa_strides y_st, int batch, int n_heads, int len,
               int head_dim, sdpa_dtype dtype, const sdpa_rope_table* rope, int pos0, void* stream) {
