@@ -203,9 +203,11 @@ int sdpa_forward_sliding(const void* q, sdpa_strides q_st,
  *                  (q_pos0 = kv_len - q_len continues the keys).  K is taken as
  *                  already rotated: rotate keys once with sdpa_rope when they
  *                  are written (a cache keeps rotated keys), not on every call.
- *                  Needs dtype F16 or BF16, rotary_dim a multiple of 64 and at
- *                  most head_dim, and 0 <= q_pos0, q_pos0 + q_len <= n_pos
- *                  (SDPA_EUNSUPPORTED / SDPA_EINVAL otherwise).
+ *                  Any dtype; rotary_dim even and at most head_dim (a multiple
+ *                  of 16 rotates 8 columns per 16-byte load, any other even
+ *                  value column by column), 16-byte aligned tables, and
+ *                  0 <= q_pos0, q_pos0 + q_len <= n_pos (SDPA_EUNSUPPORTED /
+ *                  SDPA_EINVAL otherwise).
  * Everything else as sdpa_forward; the workspace is sdpa_workspace_size_ex().
  */
 int sdpa_forward_ex(const void* q, sdpa_strides q_st,

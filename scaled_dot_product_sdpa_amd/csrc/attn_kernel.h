@@ -42,6 +42,7 @@
 #pragma once
 
 #include "attn_common.h"
+#include "rope_kernel.h"
 
 namespace sdpa_dev {
 
@@ -80,7 +81,7 @@ template <> struct OneBits<TBF16> { static constexpr uint32_t v = 0x3F80u; };
 template <> struct OneBits<TF16> { static constexpr uint32_t v = 0x3C00u; };
 template <> struct OneBits<TF32> { static constexpr uint32_t v = 0x3F800000u; };
 
-template <class TR, class C, int MASK, bool DECODE>
+template <class TR, class C, int MASK, bool DECODE, bool ROPE = false>
 __global__ __launch_bounds__(C::NT, C::OCC) void attn_tile_kernel(const Params p) {
     constexpr int ES = C::ES, EPC = C::EPC, KCH = C::KCH, BN = C::BN, D = C::D, DW = C::DW;
     constexpr int BM = 32 * C::WM;
@@ -156,6 +157,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void attn_tile_kernel(const Params p
             const int d = wd * DW + ch * KCH + hh * EPC;
             u32x4_t z = {0u, 0u, 0u, 0u};
             qf[ch] = (rv && d < D) ? *reinterpret_cast<const u32x4_t*>(qrow + (int64_t)d * ES) : z;
+        }
+        if constexpr (ROPE) {  // rotary embedding of the query row (columns < rope_dim), element by element
+            if (rv) {
+                const int64_t pos = (int64_t)p.rope_pos0 + qi;
+#pragma unroll
+                for (int ch = 0; ch < C::NCH; ++ch) {
+                    const int d = wd * DW + ch * KCH + hh * EPC;
+                    if (d < p.rope_dim) rope_fragment_elems<TR>(qf[ch], qrow, d, p.rope_dim, p.rope_cos, p.rope_sin, pos);
+                }
+            }
         }
     }
 

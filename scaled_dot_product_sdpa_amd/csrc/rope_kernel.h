@@ -25,7 +25,7 @@ struct RopeArgs {
     void* y;
     int64_t xs[4], ys[4];  // element strides, logical (b, h, l, d)
     int B, H, L, D;
-    int R;                 // rotated columns (even, multiple of 8)
+    int R;                 // rotated columns (even)
     int pos0;              // position of row 0
     const float* cos;      // [n_pos][R / 2]
     const float* sin;
@@ -81,19 +81,71 @@ __global__ __launch_bounds__(256) void rope_kernel(const RopeArgs a) {
     }
 }
 
+// One element of a 16-byte MFMA fragment (8 halves or 4 floats) as a float,
+// and back: a 16-bit element is rounded once, to nearest even (the same bits
+// RopeElem::store and TR::pack give).
+template <class TR> struct FragElem {
+    static constexpr int NE = 8;
+    static __device__ __forceinline__ float get(const u32x4_t& f, int e) {
+        return (e & 1) ? TR::unpack_hi(f[e >> 1]) : TR::unpack_lo(f[e >> 1]);
+    }
+    static __device__ __forceinline__ void set(u32x4_t& f, int e, float v) {
+        const uint32_t b = TR::pack(v, v);
+        f[e >> 1] = (e & 1) ? ((f[e >> 1] & 0x0000ffffu) | (b & 0xffff0000u)) : ((f[e >> 1] & 0xffff0000u) | (b & 0x0000ffffu));
+    }
+    static __device__ __forceinline__ float load(const char* p) {
+        return TR::unpack_lo((uint32_t)*reinterpret_cast<const uint16_t*>(p));
+    }
+};
+template <> struct FragElem<TF32> {
+    static constexpr int NE = 4;
+    static __device__ __forceinline__ float get(const u32x4_t& f, int e) { return __uint_as_float(f[e]); }
+    static __device__ __forceinline__ void set(u32x4_t& f, int e, float v) { f[e] = __float_as_uint(v); }
+    static __device__ __forceinline__ float load(const char* p) { return *reinterpret_cast<const float*>(p); }
+};
+
+// Any even R: each of a fragment's columns below R turns on its own, with its
+// partner column (h = R / 2 away) and its two table entries read one by one.
+// `frag` holds the row's columns d0 .. d0 + NE - 1 as loaded.
+template <class TR>
+__device__ __forceinline__ void rope_fragment_elems(u32x4_t& frag, const char* qrow, int d0, int R,
+                                                    const float* cos, const float* sin, int64_t pos) {
+    using E = FragElem<TR>;
+    constexpr int ES = 16 / E::NE;
+    const int h = R / 2;
+    const u32x4_t own = frag;
+#pragma unroll
+    for (int e = 0; e < E::NE; ++e) {
+        const int j = d0 + e;
+        if (j < R) {
+            const bool low = j < h;
+            const int jc = low ? j : j - h;  // table column
+            const float x = E::get(own, e);
+            const float xp = E::load(qrow + (int64_t)(low ? j + h : j - h) * ES);
+            const float c = cos[pos * h + jc], sn = sin[pos * h + jc];
+            E::set(frag, e, low ? rope_lo(x, xp, c, sn) : rope_hi(xp, x, c, sn));
+        }
+    }
+}
+
 // Rotated 16-bit MFMA fragments of one query row: frag[i] holds head-dim
-// columns d0 .. d0 + 7, d0 = i * STEP + off.  Fragments with d0 < R are
-// rebuilt from two loads of the row (their own 8 columns and the partner's,
-// h = R / 2 away) and the table entries; the rest keep what the caller
-// loaded.  Indices into `frag` stay compile-time (no register spilling).
+// columns d0 .. d0 + 7, d0 = i * STEP + off.  With R a multiple of 16 a
+// fragment lies wholly on one side of h = R / 2 and is rebuilt from two
+// 16-byte loads of the row (its own 8 columns and the partner's) and 16-byte
+// table loads; any other even R takes the element path above.  Fragments
+// with d0 >= R keep what the caller loaded.  Indices into `frag` stay
+// compile-time (no register spilling).
 template <class TR, int N, int STEP>
 __device__ __forceinline__ void rope_q_fragments(u32x4_t (&frag)[N], const char* qrow, int off, int R,
                                                  const float* cos, const float* sin, int64_t pos) {
     const int h = R / 2;
+    const bool vec = (R & 15) == 0;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         const int d0 = i * STEP + off;
-        if (d0 < R) {
+        if (d0 < R && !vec) {
+            rope_fragment_elems<TR>(frag[i], qrow, d0, R, cos, sin, pos);
+        } else if (d0 < R) {
             const bool low = d0 < h;
             const int jc = low ? d0 : d0 - h;     // table column
             const int dp = low ? d0 + h : d0 - h; // partner columns

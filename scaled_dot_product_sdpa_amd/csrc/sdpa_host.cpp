@@ -684,8 +684,7 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     p.kbase = 0;
     if (q_rope && q_rope->rotary_dim != 0) {
         const int r = q_rope->rotary_dim;
-        if (dtype == SDPA_F32) return reject(SDPA_EUNSUPPORTED);  // the fp32 kernels take no rotary prologue
-        if (r < 0 || r % 64 != 0 || r > head_dim) return reject(SDPA_EUNSUPPORTED);
+        if (r < 0 || r % 2 != 0 || r > head_dim) return reject(SDPA_EUNSUPPORTED);
         if (!q_rope->cos || !q_rope->sin || q_pos0 < 0 || (long)q_pos0 + q_len > (long)q_rope->n_pos)
             return reject(SDPA_EINVAL);
         if (((uintptr_t)q_rope->cos) % 16 != 0 || ((uintptr_t)q_rope->sin) % 16 != 0) return reject(SDPA_EUNSUPPORTED);

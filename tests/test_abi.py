@@ -179,9 +179,9 @@ def test_rope_arguments_are_checked_before_touching_the_gpu(lib):
     def ex(table, dt=2, pos0=0, d=64):
         return lib.sdpa_forward_ex(4096, st, 4096, st, 4096, st, 1 << 20, st, 2, 16, 16, 16, 16, d, d, dt, 0.125,
                                    3, None, S(0, 0, 0, 0), 0, 0, ctypes.byref(table), pos0, None, 0, None)
-    assert ex(_lib.RopeTable(32, 4096, 8192, 32)) == -2               # rotary_dim not a multiple of 64
+    assert ex(_lib.RopeTable(33, 4096, 8192, 32)) == -2               # odd rotary_dim
+    assert ex(_lib.RopeTable(-2, 4096, 8192, 32)) == -2               # negative rotary_dim
     assert ex(_lib.RopeTable(128, 4096, 8192, 32)) == -2              # rotary_dim > head_dim
-    assert ex(tab, dt=0) == -2                                        # fp32 kernels have no rotary prologue
     assert ex(_lib.RopeTable(64, None, 8192, 32)) == -1               # missing table
     assert ex(tab, pos0=17) == -1                                     # positions past the table
     assert ex(tab, pos0=-1) == -1

@@ -162,11 +162,52 @@ def test_fused_equals_rotate_then_attend(gpu_lib, D, R, lq):
     assert torch.equal(fused, two)
 
 
-def test_fused_rope_rejects_f32_and_bad_positions(gpu_lib):
+def test_fused_rope_rejects_bad_positions_and_odd_dims(gpu_lib):
     cos, sin, _, _ = tables(64, 64)
-    q = torch.zeros(1, 2, 8, 64, device="cuda")
-    with pytest.raises(gpu_lib.SdpaError):
-        gpu_lib.forward(q, q, q, rope=(cos, sin, 64))                    # no fp32 rotary prologue
-    h = q.to(torch.bfloat16)
+    h = torch.zeros(1, 2, 8, 64, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(gpu_lib.SdpaError):
         gpu_lib.forward(h, h, h, rope=(cos, sin, 64), q_pos0=60)         # rows 60..67 past a 64-row table
+    c3, s3, _, _ = tables(64, 34)
+    with pytest.raises(gpu_lib.SdpaError):
+        gpu_lib.forward(h, h, h, rope=(c3[:, :16].contiguous(), s3[:, :16].contiguous(), 33))  # odd rotary dim
+
+
+# --------------------------------------------------------------------------
+# Any even rotary dim: the 25% partial rotations of the narrow heads (R = 16,
+# 18, 20, 32 at D = 64, 72, 80, 128), a two-column one, R not a multiple of 16
+# on the wide heads, on the prefill, single-launch decode and split decode
+# kernels; and the fp32 kernels with a table.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("mask_kind", ["none", "causal", "additive"])
+@pytest.mark.parametrize("D,R", [(64, 16), (72, 18), (80, 20), (96, 24), (128, 32), (128, 2), (256, 40),
+                                 (512, 136), (72, 72)])
+def test_fused_rope_any_even_dim_prefill(gpu_lib, D, R, mask_kind):
+    c, k_rot, rope, pos0, ref = fused_case(1, 4, 2, 150, 170, D, R, "bf16", mask_kind, seed=D + 3 * R)
+    assert_parity(run_fused(c, k_rot, rope, pos0), ref, "bf16", f"fused rope prefill D={D} R={R} {mask_kind}")
+
+
+@pytest.mark.parametrize("lq", [1, 5])
+@pytest.mark.parametrize("D,R", [(64, 16), (72, 18), (128, 32), (256, 40), (512, 136), (80, 2)])
+def test_fused_rope_any_even_dim_decode(gpu_lib, D, R, lq):
+    for hkv in (2, 8):  # 2 kv heads: split + combine kernels; 8 (with 32 query heads): the single launch
+        c, k_rot, rope, pos0, ref = fused_case(1, 4 * hkv, hkv, lq, 700, D, R, "bf16", "additive", seed=D + lq)
+        route = gpu_lib.describe_route(1, lq, 700, 4 * hkv, hkv, D, torch.bfloat16, "additive")
+        assert_parity(run_fused(c, k_rot, rope, pos0), ref, "bf16",
+                      f"fused rope decode D={D} R={R} Lq={lq} Hkv={hkv} ({route.split()[0]})")
+
+
+@pytest.mark.parametrize("D,R,lq", [(72, 18, 150), (128, 32, 4), (256, 40, 1), (64, 16, 150)])
+def test_fused_any_even_dim_equals_rotate_then_attend(gpu_lib, D, R, lq):
+    c, k_rot, (cos, sin, _), pos0, _ = fused_case(1, 8, 2, lq, 300, D, R, "bf16", "causal", seed=D + R)
+    fused = run_fused(c, k_rot, (cos, sin, R), None)
+    q_rot = gpu_lib.rope(c.q.cuda(), cos, sin, R, pos0=300 - lq)
+    two = gpu_lib.forward(q_rot, k_rot.cuda(), c.v.cuda(), scale=c.scale, mask_kind="causal")
+    torch.cuda.synchronize()
+    assert torch.equal(fused, two)
+
+
+@pytest.mark.parametrize("lq,mask_kind", [(82, "none"), (82, "causal"), (3, "additive"), (1, "causal")])
+@pytest.mark.parametrize("D,R", [(64, 64), (64, 16), (128, 34)])
+def test_fused_rope_f32(gpu_lib, D, R, lq, mask_kind):
+    c, k_rot, rope, pos0, ref = fused_case(2, 4, 2, lq, 90, D, R, "f32", mask_kind, seed=D + R + lq)
+    assert_parity(run_fused(c, k_rot, rope, pos0), ref, "f32", f"fused rope f32 D={D} R={R} Lq={lq} {mask_kind}")
