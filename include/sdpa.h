@@ -207,7 +207,11 @@ int sdpa_forward_sliding(const void* q, sdpa_strides q_st,
  *                  of 16 rotates 8 columns per 16-byte load, any other even
  *                  value column by column), 16-byte aligned tables, and
  *                  0 <= q_pos0, q_pos0 + q_len <= n_pos (SDPA_EUNSUPPORTED /
- *                  SDPA_EINVAL otherwise).
+ *                  SDPA_EINVAL otherwise).  When v_head_dim == head_dim and
+ *                  rotary_dim is above 128, 128 of 128, or not a multiple of
+ *                  16 and above 32, Q is first rotated into `out` by a pass of
+ *                  its own and the attention kernels read it from there: the
+ *                  same bits as the in-kernel rotation, one more launch.
  * Everything else as sdpa_forward; the workspace is sdpa_workspace_size_ex().
  */
 int sdpa_forward_ex(const void* q, sdpa_strides q_st,

@@ -128,6 +128,58 @@ __device__ __forceinline__ void rope_fragment_elems(u32x4_t& frag, const char* q
     }
 }
 
+// The same rotation, 16 bytes at a time: one thread per (row, unit), a unit
+// being one 16-byte chunk of the low half [0, h) together with its partner
+// chunk h further on (both written), or, out of place, one chunk of the
+// pass-through columns [R, D).  Needs R a multiple of two chunks, D a whole
+// number of chunks and 16-byte aligned rows and tables (the host checks);
+// gives the bits of rope_kernel.  Grid: ceil(B * H * L * nunit / 256).
+template <class TR>
+__global__ __launch_bounds__(256) void rope_kernel_vec(const RopeArgs a, int nunit) {
+    using E = FragElem<TR>;
+    constexpr int NE = E::NE, ES = 16 / NE;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (int64_t)a.B * a.H * a.L * nunit) return;
+    const int u = (int)(t % nunit);
+    int64_t r = t / nunit;
+    const int l = (int)(r % a.L);
+    r /= a.L;
+    const int hh = (int)(r % a.H), b = (int)(r / a.H);
+    const int h = a.R / 2, nrot = h / NE;
+    const char* xr = reinterpret_cast<const char*>(a.x) +
+                     ((int64_t)b * a.xs[0] + (int64_t)hh * a.xs[1] + (int64_t)l * a.xs[2]) * ES;
+    char* yr = reinterpret_cast<char*>(a.y) + ((int64_t)b * a.ys[0] + (int64_t)hh * a.ys[1] + (int64_t)l * a.ys[2]) * ES;
+    if (u < nrot) {
+        const int j = u * NE;
+        const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(xr + (int64_t)j * ES);
+        const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(xr + (int64_t)(j + h) * ES);
+        const int64_t pos = (int64_t)a.pos0 + l;
+        float cv[NE], sv[NE];
+#pragma unroll
+        for (int q = 0; q < NE / 4; ++q) {
+            const f32x4_t c4 = *reinterpret_cast<const f32x4_t*>(a.cos + pos * h + j + 4 * q);
+            const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(a.sin + pos * h + j + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                cv[4 * q + e] = c4[e];
+                sv[4 * q + e] = s4[e];
+            }
+        }
+        u32x4_t y0 = x0, y1 = x1;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const float xa = E::get(x0, e), xb = E::get(x1, e);
+            E::set(y0, e, rope_lo(xa, xb, cv[e], sv[e]));
+            E::set(y1, e, rope_hi(xa, xb, cv[e], sv[e]));
+        }
+        *reinterpret_cast<u32x4_t*>(yr + (int64_t)j * ES) = y0;
+        *reinterpret_cast<u32x4_t*>(yr + (int64_t)(j + h) * ES) = y1;
+    } else {
+        const int j = a.R + (u - nrot) * NE;
+        *reinterpret_cast<u32x4_t*>(yr + (int64_t)j * ES) = *reinterpret_cast<const u32x4_t*>(xr + (int64_t)j * ES);
+    }
+}
+
 // Rotated 16-bit MFMA fragments of one query row: frag[i] holds head-dim
 // columns d0 .. d0 + 7, d0 = i * STEP + off.  With R a multiple of 16 a
 // fragment lies wholly on one side of h = R / 2 and is rebuilt from two

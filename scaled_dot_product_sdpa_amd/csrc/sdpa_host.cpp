@@ -600,6 +600,60 @@ int scratch_pointer(void** out) {
     return SDPA_OK;
 }
 
+// The rotary embedding of a strided [B, H, L, D] tensor into y (arguments
+// already checked): 16 bytes per thread when R is a multiple of two 16-byte
+// chunks and rows and tables are 16-byte aligned, else one thread per column.
+// Both kernels give the same bits.
+int launch_rope(const void* x, const sdpa_strides& x_st, void* y, const sdpa_strides& y_st, int batch, int n_heads,
+                int len, int head_dim, sdpa_dtype dtype, int r, int pos0, const float* cos, const float* sin,
+                hipStream_t s) {
+    const int es = elem_size(dtype), ne = 16 / es;
+    sdpa_dev::RopeArgs a{};
+    a.x = x;
+    a.y = y;
+    const int64_t xs[4] = {x_st.b, x_st.h, x_st.l, x_st.d}, ys[4] = {y_st.b, y_st.h, y_st.l, y_st.d};
+    for (int i = 0; i < 4; ++i) {
+        a.xs[i] = xs[i];
+        a.ys[i] = ys[i];
+    }
+    a.B = batch;
+    a.H = n_heads;
+    a.L = len;
+    a.D = head_dim;
+    a.R = r;
+    a.pos0 = pos0;
+    a.cos = cos;
+    a.sin = sin;
+    const bool same = x == y && x_st.b == y_st.b && x_st.h == y_st.h && x_st.l == y_st.l;
+    bool vec = r % (2 * ne) == 0 && head_dim % ne == 0 && ((uintptr_t)x) % 16 == 0 && ((uintptr_t)y) % 16 == 0 &&
+               ((uintptr_t)cos) % 16 == 0 && ((uintptr_t)sin) % 16 == 0;
+    for (int i = 0; i < 3; ++i) vec = vec && xs[i] % ne == 0 && ys[i] % ne == 0;
+    if (vec) {
+        const int nunit = r / 2 / ne + (same ? 0 : (head_dim - r) / ne);
+        if (nunit == 0) return SDPA_OK;
+        const int64_t total = (int64_t)batch * n_heads * len * nunit;
+        if ((total + 255) / 256 > 0x7fffffffLL) return SDPA_EUNSUPPORTED;
+        const dim3 grid((unsigned)((total + 255) / 256));
+        if (dtype == SDPA_F32)
+            hipLaunchKernelGGL(sdpa_dev::rope_kernel_vec<sdpa_dev::TF32>, grid, dim3(256), 0, s, a, nunit);
+        else if (dtype == SDPA_F16)
+            hipLaunchKernelGGL(sdpa_dev::rope_kernel_vec<sdpa_dev::TF16>, grid, dim3(256), 0, s, a, nunit);
+        else
+            hipLaunchKernelGGL(sdpa_dev::rope_kernel_vec<sdpa_dev::TBF16>, grid, dim3(256), 0, s, a, nunit);
+        return hip_status(hipGetLastError());
+    }
+    const int64_t total = (int64_t)batch * n_heads * len * head_dim;
+    if ((total + 255) / 256 > 0x7fffffffLL) return SDPA_EUNSUPPORTED;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (dtype == SDPA_F32)
+        hipLaunchKernelGGL(sdpa_dev::rope_kernel<float>, grid, dim3(256), 0, s, a);
+    else if (dtype == SDPA_F16)
+        hipLaunchKernelGGL(sdpa_dev::rope_kernel<_Float16>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(sdpa_dev::rope_kernel<__bf16>, grid, dim3(256), 0, s, a);
+    return hip_status(hipGetLastError());
+}
+
 int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k_st, const void* v,
                  sdpa_strides v_st, void* out, sdpa_strides o_st, int batch, int q_len, int kv_len, int n_q_heads,
                  int n_kv_heads, int head_dim, int v_head_dim, sdpa_dtype dtype, float scale, sdpa_mask_kind mask_kind,
@@ -695,6 +749,26 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         p.rope_cos = q_rope->cos;
         p.rope_sin = q_rope->sin;
     }
+    // Where the in-kernel rotation of Q costs more than a pass of its own (many
+    // fragments per lane: rotary dims above 128, a full rotation of 128; or the
+    // column-by-column path beyond 32 columns), Q is rotated into `out` first and
+    // the kernels read it from there without a table.  `out` has Q's shape when
+    // v_head_dim == head_dim, and every workgroup reads the query rows it later
+    // overwrites with their output before it writes them, so no buffer is needed.
+    const bool q_prepass =
+        p.rope_dim > 0 && v_head_dim == head_dim &&
+        (p.rope_dim > 128 || (p.rope_dim == 128 && head_dim == 128) || (p.rope_dim % 16 != 0 && p.rope_dim > 32));
+    const bool rope_k = p.rope_dim > 0 && !q_prepass;  // kernels with the rotary prologue
+    auto rotate_q_into_out = [&]() -> int {
+        if (!q_prepass) return SDPA_OK;
+        const int rs = launch_rope(q, q_st, out, o_st, batch, n_q_heads, q_len, head_dim, dtype, p.rope_dim,
+                                   p.rope_pos0, p.rope_cos, p.rope_sin, reinterpret_cast<hipStream_t>(stream));
+        if (rs != SDPA_OK) return rs;
+        p.q = out;
+        for (int i = 0; i < 4; ++i) p.qs[i] = p.os[i];
+        p.rope_dim = 0;
+        return SDPA_OK;
+    };
 
     const KernelSet* ks = kernel_set(dtype, head_dim, v_head_dim);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -720,11 +794,12 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
                                     mask_kind, st, kern, reason));
         const bool strided = !p.mask_vec && ks->full_strided[mk];
-        const launch_fn f = fp.small     ? (p.rope_dim > 0 ? ks->full_small_rope[mk] : ks->full_small[mk])
-                            : strided    ? (p.rope_dim > 0 ? ks->full_strided_rope[mk] : ks->full_strided[mk])
-                                         : (p.rope_dim > 0 ? ks->full_rope[mk] : ks->full[mk]);
+        const launch_fn f = fp.small     ? (rope_k ? ks->full_small_rope[mk] : ks->full_small[mk])
+                            : strided    ? (rope_k ? ks->full_strided_rope[mk] : ks->full_strided[mk])
+                                         : (rope_k ? ks->full_rope[mk] : ks->full[mk]);
         if (!f) return reject(SDPA_EUNSUPPORTED);
         mark(0);
+        if ((st = rotate_q_into_out()) != SDPA_OK) return reject(st);
         st = hip_status(f(p, grid, s));
         if (st != SDPA_OK) return reject(st);
         mark(1);
@@ -742,8 +817,8 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     }
     // the single-launch kernel reads mask tensors in aligned 4-key vectors with 32-bit offsets
     const bool mask_ok = !p.mask || (p.mask_vec && p.mask_span < (int64_t)0xffffffffLL);
-    const FusedPlan fpl = fused_plan(ks, batch, q_len, kv_len - p.kbase, n_q_heads, n_kv_heads, p.rope_dim > 0,
-                                     mk, mask_ok);
+    const FusedPlan fpl = fused_plan(ks, batch, q_len, kv_len - p.kbase, n_q_heads, n_kv_heads, rope_k, mk,
+                                     mask_ok);
     if (fpl.use) {
         const size_t need = fused_ws_bytes(fpl, v_head_dim);
         if (need && (!workspace || workspace_bytes < need)) return reject(SDPA_EWORKSPACE);
@@ -769,9 +844,10 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         }
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
                                     mask_kind, st, kern, reason));
-        const sdpa_host::fused_fn f = p.rope_dim > 0 ? ks->decode_fused_rope[mk] : ks->decode_fused[mk];
+        const sdpa_host::fused_fn f = rope_k ? ks->decode_fused_rope[mk] : ks->decode_fused[mk];
         if (!f) return reject(SDPA_EUNSUPPORTED);
         mark(0);
+        if ((st = rotate_q_into_out()) != SDPA_OK) return reject(st);
         st = hip_status(f(p, fg, dim3((unsigned)(fpl.groups * fpl.splits)), s));
         if (st != SDPA_OK) return reject(st);
         mark(1);
@@ -798,9 +874,10 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype, mask_kind,
                                 st, kern, reason));
     dim3 grid((unsigned)plan.splits, (unsigned)(n_kv_heads * plan.col_groups), (unsigned)batch);
-    const launch_fn f = p.rope_dim > 0 ? ks->decode_rope[mk] : ks->decode[mk];
+    const launch_fn f = rope_k ? ks->decode_rope[mk] : ks->decode[mk];
     if (!f) return reject(SDPA_EUNSUPPORTED);
     mark(0);
+    if ((st = rotate_q_into_out()) != SDPA_OK) return reject(st);
     st = hip_status(f(p, grid, s));
     if (st != SDPA_OK) return reject(st);
     mark(1);
@@ -894,31 +971,8 @@ int sdpa_rope(const void* x, sdpa_strides x_st, void* y, sdpa_strides y_st, int 
     if (!same && overlaps(y, span_bytes(n, y_st, es), x, span_bytes(n, x_st, es))) return SDPA_EINVAL;
     const int64_t total = (int64_t)batch * n_heads * len * head_dim;
     if ((total + 255) / 256 > 0x7fffffffLL) return SDPA_EUNSUPPORTED;
-    sdpa_dev::RopeArgs a{};
-    a.x = x;
-    a.y = y;
-    const int64_t xs[4] = {x_st.b, x_st.h, x_st.l, x_st.d}, ys[4] = {y_st.b, y_st.h, y_st.l, y_st.d};
-    for (int i = 0; i < 4; ++i) {
-        a.xs[i] = xs[i];
-        a.ys[i] = ys[i];
-    }
-    a.B = batch;
-    a.H = n_heads;
-    a.L = len;
-    a.D = head_dim;
-    a.R = r;
-    a.pos0 = pos0;
-    a.cos = rope->cos;
-    a.sin = rope->sin;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)((total + 255) / 256));
-    if (dtype == SDPA_F32)
-        hipLaunchKernelGGL(sdpa_dev::rope_kernel<float>, grid, dim3(256), 0, s, a);
-    else if (dtype == SDPA_F16)
-        hipLaunchKernelGGL(sdpa_dev::rope_kernel<_Float16>, grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(sdpa_dev::rope_kernel<__bf16>, grid, dim3(256), 0, s, a);
-    return hip_status(hipGetLastError());
+    return launch_rope(x, x_st, y, y_st, batch, n_heads, len, head_dim, dtype, r, pos0, rope->cos, rope->sin,
+                       reinterpret_cast<hipStream_t>(stream));
 }
 
 int sdpa_probe_stream_read(const void* src, size_t bytes, void* sink, void* stream) {

@@ -151,9 +151,10 @@ def test_graph_replay_equals_eager(gpu_lib, name, kw, kind, frag):
     assert np.abs(got - ref).max() <= tol, f"{name}: eager result off the oracle"
 
 
-@pytest.mark.parametrize("Lq", [1, 150])
-def test_graph_replay_fused_rope(gpu_lib, Lq):
-    D, R, Lk = 128, 64, 400
+@pytest.mark.parametrize("Lq,D,R", [(1, 128, 64), (150, 128, 64), (1, 256, 256), (150, 256, 256)])
+def test_graph_replay_fused_rope(gpu_lib, Lq, D, R):
+    """R = 64: the rotation inside the kernels; R = 256: a rotation pass of Q into the output first."""
+    Lk = 400
     case = si.make_case(1, 8, 2, Lq, Lk, D, seed=13, mask_kind="causal")
     c, s = oracle.rope_tables(Lk + 8, R)
     rope = (torch.from_numpy(c.astype(np.float32)).cuda(), torch.from_numpy(s.astype(np.float32)).cuda(), R)
