@@ -46,6 +46,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix
 COLD_BYTES = 600 << 20         # K/V replicas per decode run: > 2 x 256 MB Infinity Cache
+WORKLOAD_BYTES_PRIMARY = 2 * 8 * 4096 * 256 * 2  # K+V bytes of the headline decode (the ceiling reads as many)
 MAX_POOL = 16                  # host cores one GPU's share may use
 
 WORKLOADS = {
@@ -202,6 +203,10 @@ def measure(name: str, steps: int, warmup: int, eager: bool = False) -> dict:
     roof = {"bound": bound, "achieved": rate, "peak": peak, "unit": runit, "frac": rate / peak,
             "traffic": load_traffic(name), "launches_per_step": nl, "launch_ms": ms / nl,
             "work_per_launch": amount, "work_unit": unit}
+    prof = load_profiled(name)
+    if prof:  # rocprofv3 kernel durations of the same command (profiles/kernel_times.json)
+        roof["profiled"] = {"kernel_us_per_step": prof["step_kernel_us"], "frac": prof["frac_of_peak"],
+                            "kernels": {k: round(v["avg_us"], 3) for k, v in prof["kernels"].items()}}
     res = dict(config=describe(name, c), route=route, value=rate, unit=runit, ms_per_step=ms,
                eager_ms_per_step=eager_ms, replicas=nrep, roofline=roof)
     del reps
@@ -322,33 +327,138 @@ def _short(kernel: str) -> str:
     return s
 
 
-def summarize_trace(trace_csv: str, command: str) -> str:
-    """Markdown summary of a rocprofv3 kernel trace: per kernel and grid, the average duration
-    over every launch and over back-to-back launches (a launch that starts when the previous
-    one ends: the graph-replayed steps, whose durations include the launch's fixed cost)."""
+def trace_runs(trace_csv: str, steps: int):
+    """Per workload of a default bench run, from a rocprofv3 kernel trace of it: the library's kernels
+    of each workload's timed graph replay (the last `steps` launches of each kernel in that
+    workload's stretch of the trace), their average duration and the average start-to-start period.
+
+    Workloads are measured one after another, separated by host work (input generation) of
+    milliseconds; the stretches are split at gaps of more than 5 ms and named in the bench's
+    order: the primary workload, the others in WORKLOADS order, then the streaming-read ceiling."""
     rows = list(csv.DictReader(open(trace_csv)))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    stats = {}
-    prev_end = None
+    segs, cur, prev = [], [], None
     for r in rows:
-        s, e = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
-        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1)) *
-               int(r.get("Grid_Size_Z", 1)) // max(1, int(r["Workgroup_Size_X"])))
-        ent = stats.setdefault(key, {"all": [], "b2b": []})
-        ent["all"].append((e - s) / 1000.0)
-        if prev_end is not None and s - prev_end <= 500:  # within 0.5 us of the previous launch's end
-            ent["b2b"].append((e - s) / 1000.0)
-        prev_end = e
-    out = [f"Command (repo root, one MI355X, `export TMPDIR=/tmp`):", "", "```", command, "```", "",
-           "| kernel | workgroups | launches | avg us (all) | back-to-back launches | avg us (back-to-back) |",
-           "|---|---|---|---|---|---|"]
-    for (k, wg), ent in sorted(stats.items(), key=lambda x: -sum(x[1]["all"])):
-        a, bb = ent["all"], ent["b2b"]
-        if k.startswith("__amd") or k.startswith("at::") or len(a) < 3:
-            continue
-        out.append(f"| `{k}` | {wg} | {len(a)} | {sum(a) / len(a):.2f} | {len(bb)} | "
-                   f"{(sum(bb) / len(bb)) if bb else float('nan'):.2f} |")
+        s0, e0 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        if prev is not None and s0 - prev > 5_000_000:
+            segs.append(cur)
+            cur = []
+        cur.append(r)
+        prev = e0
+    segs.append(cur)
+    order = [PRIMARY] + [w for w in WORKLOADS if w != PRIMARY]
+    out, i = [], 0
+    for seg in segs:
+        ours = [r for r in seg if "sdpa_dev::" in r["Kernel_Name"]]
+        kernels = {}
+        for r in ours:
+            grid = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y") or 1) * int(r.get("Grid_Size_Z") or 1)
+            k = (_short(r["Kernel_Name"]), grid // max(1, int(r["Workgroup_Size_X"])))
+            kernels.setdefault(k, []).append(r)
+        lib = {k: v for k, v in kernels.items() if not k[0].startswith("stream_read_kernel")}
+        if lib and i < len(order):
+            out.append((order[i], _run_stats(lib, steps)))
+            i += 1
+        probe = {k: v for k, v in kernels.items() if k[0].startswith("stream_read_kernel")}
+        if probe:
+            out.append(("ceiling", _run_stats(probe, steps)))
+    return out
+
+
+def _run_stats(kernels: dict, steps: int) -> dict:
+    res = {}
+    for (k, wg), rs in kernels.items():
+        last = rs[-steps:]
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in last]
+        st = [int(r["Start_Timestamp"]) for r in last]
+        per = [(b - a) / 1000.0 for a, b in zip(st, st[1:])]
+        res[(k, wg)] = {"workgroups": wg, "launches": len(rs), "timed": len(last), "avg_us": sum(d) / len(d),
+                  "period_us": (sum(per) / len(per)) if per else None}
+    return res
+
+
+def summarize_trace(trace_csv: str, command: str, steps: int = 20) -> str:
+    """Markdown summary of a rocprofv3 kernel trace of a default bench run (see trace_runs), plus
+    profiles/kernel_times.json with the same figures keyed by the kernel sources' hash."""
+    runs = trace_runs(trace_csv, steps)
+    out = ["Command (repo root, one MI355X, `export TMPDIR=/tmp`):", "", "```", command, "```", "",
+           f"Per workload, the library's kernels of the timed graph replay (the last {steps} launches of each "
+           "kernel in that workload's part of the trace): average kernel duration and average start-to-start "
+           "period of consecutive launches. A step of a two-kernel route is the sum of its kernels.", "",
+           "| workload | kernel | workgroups | launches (timed) | avg kernel us | avg period us | "
+           "work per launch | rate from avg kernel | of peak |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    table = {}
+    for name, ks in runs:
+        tot = sum(v["avg_us"] for v in ks.values())
+        work_amt, unit, peak = None, None, BF16_PEAK_TFLOPS
+        if name in WORKLOADS:
+            c = make_case(name)
+            work_amt, unit = work(c)
+            if c.q.element_size() == 4:
+                peak = FP32_PEAK_TFLOPS
+        elif name == "ceiling":
+            work_amt, unit = float(WORKLOAD_BYTES_PRIMARY), "bytes"
+
+        def rate_of(us):
+            if work_amt is None:
+                return "", "", None
+            if unit == "bytes":
+                r = work_amt / (us * 1e-6) / 1e9
+                return f"{r:.0f} GB/s", f"{r / HBM_PEAK_GBS:.3f}", r / HBM_PEAK_GBS
+            r = work_amt / (us * 1e-6) / 1e12
+            return f"{r:.1f} TFLOP/s", f"{r / peak:.3f}", r / peak
+        wstr = "" if work_amt is None else (f"{work_amt / 1e6:.2f} MB" if unit == "bytes" else
+                                           f"{work_amt / 1e9:.3f} GFLOP")
+        for (k, wg), v in sorted(ks.items(), key=lambda x: -x[1]["avg_us"]):
+            rate, frac, _ = rate_of(v["avg_us"]) if len(ks) == 1 else ("", "", None)
+            per = f"{v['period_us']:.2f}" if v["period_us"] is not None else "-"
+            out.append(f"| {name} | `{k}` | {wg} | {v['launches']} ({v['timed']}) | {v['avg_us']:.2f} | {per} | "
+                       f"{wstr} | {rate} | {frac} |")
+        rate, frac, fv = rate_of(tot)
+        if len(ks) > 1:
+            out.append(f"| {name} | step: the kernels above | | | {tot:.2f} | | {wstr} | {rate} | {frac} |")
+        table[name] = {"kernels": {k: v for (k, _), v in ks.items()}, "step_kernel_us": tot,
+                       "work_per_step": work_amt, "work_unit": unit, "frac_of_peak": fv}
+    with open(os.path.join(ROOT, "profiles", "kernel_times.json"), "w") as f:
+        json.dump({"command": command, "kernel_hash": kernel_hash(), "steps": steps, "workloads": table}, f, indent=1)
+    # one file per workload, named for its kernel and the workload: the rows above and,
+    # where profiles/counters.json holds them for the current sources, its HBM bytes
+    counters = {}
+    cp = os.path.join(ROOT, "profiles", "counters.json")
+    if os.path.exists(cp):
+        counters = json.load(open(cp)).get("workloads", {})
+    head = out[:10]
+    for name, ks in runs:
+        main_k = max(ks.items(), key=lambda x: x[1]["avg_us"])[0][0]
+        stem = main_k.split("<")[0] + "_" + name
+        rows = [r for r in out[10:] if r.startswith(f"| {name} |")]
+        text = [f"# `{main_k}`: {name}", ""] + head + rows + [""]
+        ent = counters.get(name)
+        if ent and ent.get("kernel_hash") == kernel_hash(name) and "hbm_bytes_per_launch" in ent:
+            text += ["HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a device-to-device "
+                     "copy; profiles/counters.json):", "",
+                     f"- read {ent['hbm_read_bytes_per_launch'] / 1e6:.2f} MB, written "
+                     f"{ent['hbm_write_bytes_per_launch'] / 1e6:.2f} MB; Q+K+V {ent['qkv_bytes'] / 1e6:.2f} MB, "
+                     f"O {ent['o_bytes'] / 1e6:.2f} MB", ""]
+            text += ["```"] + ent.get("commands", []) + ["```", ""]
+        with open(os.path.join(ROOT, "profiles", stem + ".md"), "w") as f:
+            f.write("\n".join(text))
     return "\n".join(out) + "\n"
+
+
+def load_profiled(name: str):
+    """The rocprofv3 figures for a workload (profiles/kernel_times.json), if taken on the current sources."""
+    p = os.path.join(ROOT, "profiles", "kernel_times.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        data = json.load(open(p))
+    except Exception:
+        return None
+    if data.get("kernel_hash") != kernel_hash():
+        return None
+    return data.get("workloads", {}).get(name)
 
 
 def ingest_counters(pmc_dir: str, calib_bytes: int):
@@ -373,12 +483,16 @@ def ingest_counters(pmc_dir: str, calib_bytes: int):
         v = per_dispatch(f"{counter}_copy", counter, lambda k: "copy" in k.lower())
         big = max(v.values()) if v else 0.0
         out["calibration"][counter] = {"copy_bytes": calib_bytes, "counter_kib_per_copy": big,
-                                       "factor": calib_bytes / (big * 1024.0) if big else None}
+                                       "factor": calib_bytes / (big * 1024.0) if big else None,
+                                       "command": f"rocprofv3 --pmc {counter} -d gpurun_out/prof/pmc/{counter}_copy -o run "
+                                                  f"-f csv -- python3 bench.py --profile-copy {calib_bytes >> 20} --steps 5"}
     for d in sorted(glob.glob(os.path.join(pmc_dir, "FETCH_SIZE_*"))):
         name = os.path.basename(d)[len("FETCH_SIZE_"):]
         if name == "copy" or name not in WORKLOADS:
             continue
-        ent = {"kernel_hash": kernel_hash(name)}
+        ent = {"kernel_hash": kernel_hash(name),
+               "commands": [f"rocprofv3 --pmc {c} -d gpurun_out/prof/pmc/{c}_{name} -o run -f csv -- python3 bench.py "
+                            f"--profile-run --workload {name} --steps 5" for c in ("FETCH_SIZE", "WRITE_SIZE")]}
         for counter, key in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
             v = per_dispatch(f"{counter}_{name}", counter, lambda k: "sdpa_dev" in k)
             if not v:
@@ -422,7 +536,7 @@ def main():
     a = ap.parse_args()
 
     if a.summarize_trace:
-        print(summarize_trace(*a.summarize_trace))
+        print(summarize_trace(a.summarize_trace[0], a.summarize_trace[1], a.steps if a.steps != 200 else 20))
         return
     if a.ingest_counters:
         res = ingest_counters(a.ingest_counters[0], int(a.ingest_counters[1]) << 20)
