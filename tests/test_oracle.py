@@ -162,6 +162,37 @@ def test_probability_rows_sum_to_one_and_are_nonnegative():
         assert (p >= 0).all()
 
 
+def test_attention_weights_group_query_heads_by_consecutive_runs():
+    """Query head h reads kv head h // n_rep (consecutive runs of n_rep heads share a kv head):
+    kv head 0 has identical keys (uniform weights), kv head 1 one key far above the rest (a
+    one-hot row).  A mapping h % Hkv would give heads 1 and 2 the other kv head's pattern."""
+    Lk, D = 6, 4
+    q = np.ones((1, 4, 2, D))
+    k = np.zeros((1, 2, Lk, D))
+    k[0, 1, 3] = 50.0
+    p = oracle.attention_weights(q, k, 1.0)
+    for h in (0, 1):
+        np.testing.assert_allclose(p[0, h], 1.0 / Lk, atol=1e-15)
+    for h in (2, 3):
+        np.testing.assert_allclose(p[0, h, :, 3], 1.0, atol=1e-12)
+        np.testing.assert_allclose(np.delete(p[0, h], 3, axis=-1), 0.0, atol=1e-12)
+
+
+def test_rope_tables_are_the_base_10000_angles():
+    """cos/sin of angle(pos, j) = pos * 10000^(-2j/R): at pos 1 column j's angle is the j-th power of
+    10000^(-2/R) (R = 64: 0.74989420933...), the angle grows linearly with the position, and column 0
+    turns one radian per position (cos 1 = 0.5403023058681398, sin 1 = 0.8414709848078965)."""
+    c, s_ = oracle.rope_tables(9, 64)
+    assert c.shape == s_.shape == (9, 32)
+    assert c[1, 0] == pytest.approx(0.5403023058681398, abs=1e-15)
+    assert s_[1, 0] == pytest.approx(0.8414709848078965, abs=1e-15)
+    ang = np.arctan2(s_, c)
+    np.testing.assert_allclose(ang[0], 0.0, atol=0)
+    ratio = ang[1, 1:] / ang[1, :-1]
+    np.testing.assert_allclose(ratio, 0.7498942093324559, rtol=1e-12)
+    np.testing.assert_allclose(ang[3], 3.0 * ang[1], rtol=1e-12)  # below pi: no wrap
+
+
 def test_causal_row0_is_v0_and_single_key_is_v0():
     q, k, v = _rand((1, 3, 6, 4), 1), _rand((1, 3, 6, 4), 2), _rand((1, 3, 6, 4), 3)
     out = oracle.sdpa(q, k, v, 2.0, "causal")
