@@ -152,7 +152,12 @@ typedef struct {
  *                  that uses the workspace (allocate it zero-filled once) and
  *                  every call leaves them zero again; the rest needs no
  *                  initialisation and is garbage afterwards.  Calls that
- *                  share a workspace must be ordered on one stream.
+ *                  share a workspace must be ordered on one stream.  The full
+ *                  kernel uses the bytes after the counters for the lane masks
+ *                  of a BOOLEAN mask (one bit per mask element, built by a
+ *                  pre-pass and read by every head that shares the mask) when
+ *                  they fit; otherwise it reads the mask bytes themselves, with
+ *                  the same result bit for bit.
  *   stream         hipStream_t as void*.
  * Returns SDPA_OK or a negative status; nothing is enqueued on error.
  */
@@ -304,12 +309,17 @@ int sdpa_describe_route_ex(int batch, int q_len, int kv_len, int n_q_heads, int 
 /*
  * sdpa_workspace_size -- bytes of workspace sdpa_forward needs for this shape
  * (the 2-pass vector kernel of mlx issue #3885, "Current routing", keeps one
- * partial result per key split): 0 for the full kernel and for a vector call
- * whose key range is not split; otherwise 32768 bytes of arrival counters
- * (zero-initialised once, see sdpa_forward) followed by the per-split partial
- * results (an fp32 output row plus running max and sum, per split, query head
- * and query row).  An upper bound over every mask kind, mask layout, sliding
- * window and rotary option for the same shape, on the current device.
+ * partial result per key split): 0 for a vector call whose key range is not
+ * split; otherwise 32768 bytes of arrival counters (zero-initialised once, see
+ * sdpa_forward) followed by the per-split partial results (an fp32 output row
+ * plus running max and sum, per split, query head and query row).  An upper
+ * bound over every mask kind, mask layout, sliding window and rotary option
+ * for the same shape, on the current device.  For the full kernel: 0 where it
+ * reads boolean masks as bytes (head dims above 128, fp32), else the counters
+ * plus the lane masks of one boolean mask shared by every batch and head,
+ * ceil(q_len / 32) * ceil(kv_len / 64) * 256 bytes; a mask that differs per
+ * batch or head needs that many per (batch, head) and runs on its bytes when
+ * the workspace is smaller.
  * Returns 0 for unsupported shapes as well.
  */
 size_t sdpa_workspace_size(int batch, int q_len, int kv_len, int n_q_heads, int n_kv_heads,

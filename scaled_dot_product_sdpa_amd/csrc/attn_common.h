@@ -71,6 +71,11 @@ struct Params {
     int rope_pos0;
     const float* rope_cos;
     const float* rope_sin;
+    // boolean mask as lane words (prefill, head dim <= 128; mask_bits.h): the 64 words
+    // of (b, h, 32-row block rb, key tile kt) start at b * mb_b + h * mb_h + rb * mb_rb
+    // + 64 kt (mb_b, mb_h 0 where the mask is broadcast)
+    const uint32_t* mask_bits;
+    int mb_b, mb_h, mb_rb, mb_pad;
 };
 
 template <class To, class From>
@@ -193,6 +198,34 @@ __device__ __forceinline__ void buffer_load16_lds_so(__amdgpu_buffer_rsrc_t r, v
                                                      uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
+#endif
+}
+// The same two loads issued from inline assembly, unseen by the compiler's
+// wait-count pass.  That pass takes every ds_read_b64_tr_b16 as aliasing
+// every LDS DMA in flight and puts an s_waitcnt vmcnt(0) in front of the
+// first one: a P V step would wait for the NEXT tile's loads, and the
+// prefetch would overlap only the score half of a tile.  The kernels that
+// use these order their DMA themselves: each tile starts with an explicit
+// vmcnt(0) and a barrier before any wave reads it, and a stage is refilled
+// only after that barrier, once every wave is done reading it.  The loads
+// have no register results (nothing for the compiler to track); M0 carries
+// the LDS base, with the one wait state the DMA needs after writing it.
+// Compiler-issued vector loads newer than these get waits counted without
+// them, which only makes those waits stricter.
+__device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
+#endif
+}
+__device__ __forceinline__ void dma16_lds_so(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r),
+                 "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(m0)
+                 : "memory");
 #endif
 }
 

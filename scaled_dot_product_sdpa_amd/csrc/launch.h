@@ -42,6 +42,10 @@ struct KernelSet {
     // handles both layouts)
     launch_fn full_strided[sdpa_dev::MASK_VARIANTS];
     launch_fn full_strided_rope[sdpa_dev::MASK_VARIANTS];
+    // prefill with a boolean mask given as precomputed lane masks
+    // (Params::mask_bits; null where not built)
+    launch_fn full_bits;
+    launch_fn full_bits_rope;
     // 16-bit decode in one launch (split keys merged in L2 by the last
     // workgroup of each group), by V column slices (index VS - 1; null where
     // not built) and mask variant

@@ -72,12 +72,16 @@ template <bool B> struct PfTag { static constexpr bool value = B; };
 
 // SMASK: the mask tensor's keys are not 4-element aligned runs (mask_vec == 0);
 // its elements are loaded one by one.
-template <class TR, class C, int MASK, bool ROPE = false, bool SMASK = false>
+// BITS (MASK_BOOL only): the mask comes as precomputed lane masks (mask_bits.h,
+// Params::mask_bits), one v_cndmask per score and no mask-tensor loads.
+template <class TR, class C, int MASK, bool ROPE = false, bool SMASK = false, bool BITS = false>
 __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) {
     constexpr int D = C::D, BN = C::BN, BM = C::BM;
     constexpr float NEG_INF = -__builtin_inff();
     constexpr float kRescale = 8.0f;
     constexpr bool HAS_MT = (MASK == MASK_ADD16 || MASK == MASK_ADD32 || MASK == MASK_BOOL);
+    constexpr bool LOADS = HAS_MT && !BITS;  // mask-tensor elements loaded by the kernel
+    static_assert(!BITS || (MASK == MASK_BOOL && !SMASK && C::BN == 64), "lane masks: boolean, 64-key tiles");
     __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
     const int tid = threadIdx.x, lane = tid & 63, wm = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -205,8 +209,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
                 const int blk = (u * C::WM + wm) * 64 * 16;  // LDS byte offset of this instruction's 64 slots
                 if (blk >= C::SLOTS * 16) break;
                 if (sok[u]) {
-                    buffer_load16_lds(krs, kt_lds + blk, kofs[u] + kb0);
-                    buffer_load16_lds(vrs, vt_lds + blk, vofs[u] + vb0);
+                    dma16_lds(krs, kt_lds + blk, kofs[u] + kb0);
+                    dma16_lds(vrs, vt_lds + blk, vofs[u] + vb0);
                 }
             }
         };
@@ -217,15 +221,24 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         // every group is one branch-free vector load (or four scalar ones).
         constexpr int MES = MASK == MASK_BOOL ? 1 : (MASK == MASK_ADD16 ? 2 : 4);
         const int q0c = min(qmin, p.Lq - 1), qic = min(qi, p.Lq - 1);
-        const int64_t mbase = HAS_MT ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)q0c * p.ms[2] : 0;
-        const uint32_t mlane = HAS_MT ? (uint32_t)((qic - q0c) * p.ms[2]) : 0u;
-        const int64_t mleft = HAS_MT ? p.mask_span - mbase * MES : 0;
+        const int64_t mbase = LOADS ? (int64_t)b * p.ms[0] + (int64_t)qh * p.ms[1] + (int64_t)q0c * p.ms[2] : 0;
+        const uint32_t mlane = LOADS ? (uint32_t)((qic - q0c) * p.ms[2]) : 0u;
+        const int64_t mleft = LOADS ? p.mask_span - mbase * MES : 0;
         const __amdgpu_buffer_rsrc_t mrs =
-            make_rsrc(HAS_MT ? reinterpret_cast<const char*>(p.mask) + mbase * MES : nullptr,
+            make_rsrc(LOADS ? reinterpret_cast<const char*>(p.mask) + mbase * MES : nullptr,
                       (uint32_t)(mleft > 0xffffffffLL ? 0xffffffffLL : mleft));
-        typename MaskRaw<MASK>::type mr[HAS_MT ? C::NKB : 1][4];
+        typename MaskRaw<MASK>::type mr[LOADS ? C::NKB : 1][4];
+        // lane words of this wave's 32-row block (BITS): 64 per key tile, one per lane,
+        // loaded a tile ahead like the mask bytes
+        uint32_t mw = 0;
+        const __amdgpu_buffer_rsrc_t wrs =
+            make_rsrc(BITS ? p.mask_bits + (int64_t)b * p.mb_b + (int64_t)qh * p.mb_h + (int64_t)(qmin / 32) * p.mb_rb
+                           : nullptr,
+                      BITS ? (uint32_t)(((p.Lk + BN - 1) / BN) * 256) : 0u);
         auto load_mask = [&](int kt) {
-            if constexpr (HAS_MT) {
+            if constexpr (BITS)
+                mw = __builtin_amdgcn_raw_buffer_load_b32(wrs, (uint32_t)((kt / BN) * 256 + lane * 4), 0, 0);
+            if constexpr (LOADS) {
                 if constexpr (!SMASK) {
     #pragma unroll
                     for (int kb = 0; kb < C::NKB; ++kb)
@@ -356,6 +369,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
             constexpr bool MASKED = decltype(masked_tag)::value, TAIL = decltype(tail_tag)::value;
             const int kt = it * BN, stage = it & 1;
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if constexpr (MASKED && BITS) asm volatile("" : "+v"(mw));
+            if constexpr (MASKED && LOADS) {
+                // this tile's mask registers arrived with the wait above; an asm use says so
+                // to the compiler, which would otherwise wait for them where they are read,
+                // after the next tile's loads went out, and so for those loads as well
+    #pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+    #pragma unroll
+                    for (int a4 = 0; a4 < 4; ++a4) asm volatile("" : "+v"(mr[kb][a4]));
+            }
             __syncthreads();  // tile `it` is in LDS; every wave is done with the other stage
             if (it + 1 < ntiles) issue_tile(kt + BN, stage ^ 1);
             f32x16_t sacc[C::NKB];
@@ -385,6 +408,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
                                 const int j = kt + kb * 32 + 8 * a4 + 4 * hh + r;
                                 float x = sacc[kb][4 * a4 + r];
                                 if constexpr (!RAW) x *= c_scale;
+                                if constexpr (BITS) {  // bit 16 kb + 4 a4 + r: this lane's (row, key j)
+                                    // all ones where it attends, else zero; then x or -inf bit by bit
+                                    const uint32_t keep =
+                                        (uint32_t)__builtin_amdgcn_sbfe((int)mw, kb * 16 + a4 * 4 + r, 1);
+                                    const float y = __uint_as_float((__float_as_uint(x) & keep) |
+                                                                    (__float_as_uint(NEG_INF) & ~keep));
+                                    sacc[kb][4 * a4 + r] = y;
+                                    mtile = fmaxf(mtile, y);
+                                    continue;
+                                }
                                 bool ok = true;
                                 if constexpr (TAIL) ok = j < kend;
                                 if constexpr (ADD)

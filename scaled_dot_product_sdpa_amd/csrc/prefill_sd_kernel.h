@@ -193,8 +193,16 @@ __global__ __launch_bounds__(C::NT, C::WPE) void prefill_sd_kernel(const Params 
                     vk = (uint32_t)(lane / C::KC) * kstep + cb;
                     vv = (uint32_t)(lane / C::KC) * vstep + cb;
                 }
-                buffer_load16_lds_so(krs, kl + ins * 1024, vk, (uint32_t)(kt + r0) * kstep);
-                buffer_load16_lds_so(vrs, vl + ins * 1024, vv, (uint32_t)(kt + r0) * vstep);
+                // a mask tensor's groups are loaded at the top of the tile that uses them,
+                // before these: the compiler's count of the loads after them lets it wait
+                // for the groups alone, so those variants keep the loads it can see
+                if constexpr (HAS_MT) {
+                    buffer_load16_lds_so(krs, kl + ins * 1024, vk, (uint32_t)(kt + r0) * kstep);
+                    buffer_load16_lds_so(vrs, vl + ins * 1024, vv, (uint32_t)(kt + r0) * vstep);
+                } else {
+                    dma16_lds_so(krs, kl + ins * 1024, vk, (uint32_t)(kt + r0) * kstep);
+                    dma16_lds_so(vrs, vl + ins * 1024, vv, (uint32_t)(kt + r0) * vstep);
+                }
             }
         };
 

@@ -22,6 +22,7 @@
 
 #include "attn_kernel.h"
 #include "decode_fused_kernel.h"
+#include "mask_bits.h"
 #include "launch.h"
 #include "rope_kernel.h"
 #include "stream_probe.h"
@@ -194,6 +195,14 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // single-launch kernel (zero before and after every call); the split + combine
 // kernels place their partial results after them and never touch them.
 constexpr size_t kCounterBytes = (size_t)sdpa_dev::kFusedCounterWords * 4;
+
+// Lane masks of a boolean mask for the head-dim <= 128 prefill kernel
+// (mask_bits.h), per (mask batch, mask head): 32 words per (32-row block,
+// 64-key tile).  They too sit after the arrival words, which a workspace
+// shared with decode calls must keep zero.
+size_t mask_bits_bytes(int q_len, int kv_len) {
+    return (size_t)((q_len + 31) / 32) * (size_t)((kv_len + 63) / 64) * sdpa_dev::kMaskBitsWords * sizeof(uint32_t);
+}
 
 // (a single split of the 16-bit split kernel writes the output itself: no workspace)
 size_t decode_ws_bytes(int batch, int q_len, int hq, int d, long splits, sdpa_dtype dt) {
@@ -474,10 +483,12 @@ size_t sdpa_workspace_size_ex(int batch, int q_len, int kv_len, int n_q_heads, i
                               int v_head_dim, sdpa_dtype dtype) {
     sdpa_kernel k;
     if (select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype, SDPA_MASK_NONE, &k,
-               nullptr) != SDPA_OK ||
-        k != SDPA_KERNEL_VECTOR)
+               nullptr) != SDPA_OK)
         return 0;
     const KernelSet* ks = kernel_set(dtype, head_dim, v_head_dim);
+    // prefill: room for the lane masks of a boolean mask shared by every batch
+    // and head (a per-head mask needs more and otherwise runs on the bytes)
+    if (k != SDPA_KERNEL_VECTOR) return (ks && ks->full_bits) ? kCounterBytes + mask_bits_bytes(q_len, kv_len) : 0;
     // an upper bound over every mask kind, window and rotary option: the
     // single-launch plan (its split count only grows with the key count), and
     // the split + combine plan's largest split count
@@ -794,12 +805,49 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         log_route_once(route_string(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype,
                                     mask_kind, st, kern, reason));
         const bool strided = !p.mask_vec && ks->full_strided[mk];
-        const launch_fn f = fp.small     ? (rope_k ? ks->full_small_rope[mk] : ks->full_small[mk])
+        // a boolean mask goes in as lane masks when the workspace holds them (one
+        // pass over the mask, shared by every head that reads it)
+        const int bm = (mask_kind == SDPA_MASK_BOOLEAN && p.ms[0] != 0) ? batch : 1;
+        const int hm = (mask_kind == SDPA_MASK_BOOLEAN && p.ms[1] != 0) ? n_q_heads : 1;
+        const size_t bits_need = mask_bits_bytes(q_len, kv_len) * (size_t)bm * (size_t)hm;
+        // (word offsets per mask head and batch are ints: under 2^31 words)
+        const bool bits = mask_kind == SDPA_MASK_BOOLEAN && !fp.small && ks->full_bits && workspace &&
+                          workspace_bytes >= kCounterBytes + bits_need && ((uintptr_t)workspace) % 256 == 0 &&
+                          bits_need < ((size_t)1 << 34);
+        char* const bits_at = reinterpret_cast<char*>(workspace) + kCounterBytes;
+        if (bits && (overlaps(out, oq, bits_at, bits_need) || overlaps(q, sq, bits_at, bits_need) ||
+                     overlaps(k, sk, bits_at, bits_need) || overlaps(v, sv, bits_at, bits_need) ||
+                     overlaps(p.mask, (size_t)p.mask_span, bits_at, bits_need)))
+            return reject(SDPA_EINVAL);
+        const launch_fn f = bits         ? (rope_k ? ks->full_bits_rope : ks->full_bits)
+                            : fp.small   ? (rope_k ? ks->full_small_rope[mk] : ks->full_small[mk])
                             : strided    ? (rope_k ? ks->full_strided_rope[mk] : ks->full_strided[mk])
                                          : (rope_k ? ks->full_rope[mk] : ks->full[mk]);
         if (!f) return reject(SDPA_EUNSUPPORTED);
         mark(0);
         if ((st = rotate_q_into_out()) != SDPA_OK) return reject(st);
+        if (bits) {
+            const int rbn = (q_len + 31) / 32, ktn = (kv_len + 63) / 64;
+            sdpa_dev::MaskBitsArgs a{};
+            a.mask = reinterpret_cast<const uint8_t*>(p.mask);
+            for (int i = 0; i < 4; ++i) a.ms[i] = p.ms[i];
+            a.bits = reinterpret_cast<uint32_t*>(bits_at);
+            a.Bm = bm;
+            a.Hm = hm;
+            a.Lq = q_len;
+            a.Lk = kv_len;
+            a.RB = rbn;
+            a.KT = ktn;
+            a.vec = p.mask_vec;
+            const int64_t units = (int64_t)bm * hm * rbn * ktn;
+            hipLaunchKernelGGL(sdpa_dev::mask_bits_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, a);
+            if ((st = hip_status(hipGetLastError())) != SDPA_OK) return reject(st);
+            const int64_t per_rb = (int64_t)ktn * sdpa_dev::kMaskBitsWords;
+            p.mask_bits = a.bits;
+            p.mb_rb = (int)per_rb;
+            p.mb_h = hm > 1 ? (int)(per_rb * rbn) : 0;
+            p.mb_b = bm > 1 ? (int)(per_rb * rbn * hm) : 0;
+        }
         st = hip_status(f(p, grid, s));
         if (st != SDPA_OK) return reject(st);
         mark(1);
@@ -940,9 +988,17 @@ int sdpa_forward_noalloc(const void* q, sdpa_strides q_st, const void* k, sdpa_s
                          int window, const sdpa_rope_table* q_rope, int q_pos0, void* stream) {
     g_counters[0].fetch_add(1, std::memory_order_relaxed);
     if (mask_kind == SDPA_MASK_SLIDING && window < 1) return reject(SDPA_EINVAL);
-    const size_t need = sdpa_workspace_size_ex(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim,
-                                               dtype);
-    if (need > kScratchBytes) return reject(SDPA_EWORKSPACE);
+    size_t need = sdpa_workspace_size_ex(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype);
+    if (need > kScratchBytes) {
+        // a prefill's workspace only speeds up boolean masks (lane masks): run without it
+        sdpa_kernel kk;
+        if (select(batch, q_len, kv_len, n_q_heads, n_kv_heads, head_dim, v_head_dim, dtype, mask_kind, &kk,
+                   nullptr) == SDPA_OK &&
+            kk == SDPA_KERNEL_FULL)
+            need = 0;
+        else
+            return reject(SDPA_EWORKSPACE);
+    }
     void* ws = nullptr;
     if (need) {
         const int st = scratch_pointer(&ws);

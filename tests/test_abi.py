@@ -104,7 +104,13 @@ def test_describe_route(lib):
 
 def test_workspace_size(lib):
     align = lambda x: (x + 255) // 256 * 256
-    assert sdpa.workspace_size(1, 100, 100, 8, 2, 64, 2) == 0          # full kernel needs none
+    # prefill: the 32 KiB of arrival words every workspace starts with, then room for the lane
+    # masks of a boolean mask shared by batch and heads, 32 words (8 bytes) per 32-row block and
+    # 64-key tile, where the 16-bit head-dim <= 128 kernel runs
+    assert sdpa.workspace_size(1, 100, 100, 8, 2, 64, 2) == 32768 + 4 * 2 * 32 * 8
+    assert sdpa.workspace_size(1, 8192, 8192, 16, 16, 72, 2) == 32768 + 256 * 128 * 256   # c4: 8 MiB
+    assert sdpa.workspace_size(1, 100, 100, 8, 2, 64, 0) == 0           # fp32 prefill: none
+    assert sdpa.workspace_size(1, 100, 100, 8, 2, 256, 2) == 0          # the wide-head kernel: none
     # single-launch decode: 32 KiB of arrival words, then per (group, split, row) one
     # fp32 partial row of the group's V columns and its (max, sum)
     # (a mask tensor without aligned 4-key runs takes the split + combine kernels: the size covers both)

@@ -387,3 +387,66 @@ def test_decode_forced_single_split(gpu_lib, monkeypatch, D, dv, mask_kind):
     c = si.make_case(1, 8, 2, 3, 900, D, dtype="bf16", layout="bhld", mask_kind=mask_kind, seed=D + 3, dv=dv,
                      mask_shape="qk", mask_p=0.3, window=50 if mask_kind == "sliding" else None)
     assert_parity(run_gpu(c), oracle_out(c), "bf16", f"decode single split D={D} {mask_kind}")
+
+
+# --------------------------------------------------------------------------
+# Boolean masks as precomputed lane masks (the head-dim <= 128 prefill kernel,
+# with the workspace the library asks for) against the same call on the mask
+# bytes (a workspace too small for the lane masks): the same bits, and the
+# oracle.  Shared, per-head and per-batch masks; ragged Lq / Lk; strided mask
+# layouts; the rotary variant.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("D,B,Hq,Hkv,Lq,Lk,shape", [(72, 1, 4, 2, 300, 333, "qk"), (64, 2, 4, 4, 129, 65, "full"),
+                                                    (128, 1, 8, 2, 100, 1000, "qk"), (96, 2, 2, 1, 40, 4100, "full"),
+                                                    (80, 1, 3, 1, 1030, 300, "qk")])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_boolean_lane_masks_equal_the_byte_path(gpu_lib, D, B, Hq, Hkv, Lq, Lk, shape, dtype):
+    c = si.make_case(B, Hq, Hkv, Lq, Lk, D, dtype=dtype, mask_kind="boolean", mask_shape=shape, mask_p=0.3,
+                     seed=D + Lq)
+    q, k, v, m = to_device(c)
+    need = gpu_lib.workspace_size(B, Lq, Lk, Hq, Hkv, D, q.dtype) * (B * Hq if shape == "full" else 1)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    tiny = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    bits = gpu_lib.forward(q, k, v, scale=c.scale, mask=m, mask_kind="boolean", workspace=ws)
+    byte = gpu_lib.forward(q, k, v, scale=c.scale, mask=m, mask_kind="boolean", workspace=tiny)
+    torch.cuda.synchronize()
+    assert torch.equal(bits, byte)
+    assert_parity(bits, oracle_out(c), dtype, f"boolean lane masks D={D} {shape}")
+
+
+def test_boolean_lane_masks_strided_mask_and_rope(gpu_lib):
+    D, Lq, Lk, R = 72, 200, 260, 18
+    c = si.make_case(1, 4, 2, Lq, Lk, D, dtype="bf16", mask_kind="boolean", mask_shape="qk", mask_p=0.2, seed=5)
+    q, k, v, m = to_device(c)
+    dm = c.mask.transpose(-1, -2).contiguous().cuda().transpose(-1, -2)  # keys strided
+    import oracle
+    cos, sin = (torch.from_numpy(t.astype(np.float32)).cuda() for t in oracle.rope_tables(Lk + 4, R))
+    ws = torch.zeros(gpu_lib.workspace_size(1, Lq, Lk, 4, 2, D, q.dtype), dtype=torch.uint8, device="cuda")
+    tiny = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    for mask in (m, dm):
+        for rope in (None, (cos, sin, R)):
+            a = gpu_lib.forward(q, k, v, scale=c.scale, mask=mask, mask_kind="boolean", workspace=ws, rope=rope)
+            b = gpu_lib.forward(q, k, v, scale=c.scale, mask=mask, mask_kind="boolean", workspace=tiny, rope=rope)
+            torch.cuda.synchronize()
+            assert torch.equal(a, b), f"rope={rope is not None} strided={mask is dm}"
+
+
+def test_boolean_prefill_then_decode_on_one_workspace(gpu_lib):
+    """The lane masks sit after the workspace's arrival words: a boolean prefill leaves them zero,
+    and a single-launch decode on the same workspace afterwards is still right."""
+    pre = si.make_case(1, 4, 2, 300, 300, 64, dtype="bf16", mask_kind="boolean", mask_shape="qk", mask_p=0.3, seed=8)
+    dec = si.make_case(1, 32, 8, 1, 700, 64, dtype="bf16", mask_kind="additive", seed=9)
+    assert "vector-fused" in gpu_lib.describe_route(1, 1, 700, 32, 8, 64, torch.bfloat16, "additive")
+    n = max(gpu_lib.workspace_size(1, 300, 300, 4, 2, 64, torch.bfloat16),
+            gpu_lib.workspace_size(1, 1, 700, 32, 8, 64, torch.bfloat16))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        q, k, v, m = to_device(pre)
+        a = gpu_lib.forward(q, k, v, scale=pre.scale, mask=m, mask_kind="boolean", workspace=ws)
+        torch.cuda.synchronize()
+        assert not ws[:COUNTER_BYTES].any(), "the prefill wrote into the arrival words"
+        q, k, v, m = to_device(dec)
+        b = gpu_lib.forward(q, k, v, scale=dec.scale, mask=m, mask_kind="additive", workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(a, oracle_out(pre), "bf16", "boolean prefill")
+        assert_parity(b, oracle_out(dec), "bf16", "decode after a boolean prefill")
