@@ -52,9 +52,12 @@ struct PfCfg {
     static constexpr bool PAIRS = true;               // causal: two row tiles per workgroup (see the kernel)
     static constexpr int SLOTS = BN * RC;             // 16-byte slots per tile
     static constexpr int NLD = (SLOTS + NT - 1) / NT; // load instructions per thread per tile (K or V)
-    // K0, V0, K1, V1; padded rows: transposed V reads of the last row may run
-    // up to 32 bytes past it (head-dim columns beyond D, never stored)
-    static constexpr int LDS = 4 * TILEB + (SWZ ? 0 : 64);
+    // V0, K0, V1, K1: transposed V reads of a tile's last row may run up to 32
+    // bytes past it (head-dim columns beyond D, never stored), into the K tile
+    // after it, so the block needs no padding (head dim 72: 40 KiB, a quarter
+    // of a CU's LDS).
+    static constexpr int LDS = 4 * TILEB;
+    static constexpr int KOFF0 = TILEB, VOFF0 = 0;    // stage s: + 2 s TILEB
     static_assert(D % 8 == 0 && D <= 128, "head dim");
     static_assert(BN % 32 == 0, "key tile");
     static_assert(!ONES || (D % 32) <= 16, "ones column must sit in the spare chunk");
@@ -182,8 +185,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         // ---- spare chunks: K rows 0, V rows (1 at column D if ONES, else 0) ----
         if constexpr (!C::SWZ)
         for (int r = tid; r < 4 * BN; r += C::NT) {
-            const int tile = r / BN, row = r % BN;  // tiles K0, V0, K1, V1
-            const bool is_v = tile & 1;
+            const int tile = r / BN, row = r % BN;  // tiles V0, K0, V1, K1
+            const bool is_v = !(tile & 1);
             u32x4_t z = {0u, 0u, 0u, 0u};
             if (is_v && C::ONES) z[0] = OneBits<TR>::v;
             *reinterpret_cast<u32x4_t*>(smem + tile * C::TILEB + row * C::ROWB + C::KC * 16) = z;
@@ -201,8 +204,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
             vofs[u] = (uint32_t)row * vstep32 + (uint32_t)(ch * 16);
         }
         auto issue_tile = [&](int kt, int stage) {
-            char* kt_lds = smem + (2 * stage) * C::TILEB;
-            char* vt_lds = smem + (2 * stage + 1) * C::TILEB;
+            char* kt_lds = smem + 2 * stage * C::TILEB + C::KOFF0;
+            char* vt_lds = smem + 2 * stage * C::TILEB + C::VOFF0;
             const uint32_t kb0 = (uint32_t)kt * kstep32, vb0 = (uint32_t)kt * vstep32;
     #pragma unroll
             for (int u = 0; u < C::NLD; ++u) {
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         // ahead of their MFMAs (scheduling fences keep them there)
         constexpr int LA = C::LA;
         auto scores = [&](int stage, f32x16_t (&sacc)[C::NKB]) {
-            const char* kt_lds = smem + (2 * stage) * C::TILEB;
+            const char* kt_lds = smem + 2 * stage * C::TILEB + C::KOFF0;
             constexpr int N = C::NKB * C::NCH;
             auto rd = [&](int i) {
                 return *reinterpret_cast<const u32x4_t*>(kt_lds + (i / C::NCH) * 32 * C::ROWB + koff[i % C::NCH]);
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
                 }
             if constexpr (!C::ONES) l_run += lsum;
             // O^T += V^T P^T; V^T operands via transposed LDS reads of the row-major V tile
-            const char* vt_lds = smem + (2 * stage + 1) * C::TILEB;
+            const char* vt_lds = smem + 2 * stage * C::TILEB + C::VOFF0;
             u32x4_t bf[C::NKB][2];
     #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb)
