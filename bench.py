@@ -128,8 +128,11 @@ def work(c) -> tuple[float, str]:
 
 
 def launches_per_step(route: str) -> int:
-    """Kernel launches one call makes: the split + combine decode route makes two."""
+    """Kernel launches one call makes: the split + combine decode route makes two, and so does a
+    boolean-mask prefill that builds lane words first."""
     if route.startswith("vector ") and "splits=1 " not in route:
+        return 2
+    if "lane-words+prepass" in route:
         return 2
     return 1
 
@@ -440,7 +443,11 @@ def summarize_trace(trace_csv: str, command: str, steps: int = 20) -> str:
                      "copy; profiles/counters.json):", "",
                      f"- read {ent['hbm_read_bytes_per_launch'] / 1e6:.2f} MB, written "
                      f"{ent['hbm_write_bytes_per_launch'] / 1e6:.2f} MB; Q+K+V {ent['qkv_bytes'] / 1e6:.2f} MB, "
-                     f"O {ent['o_bytes'] / 1e6:.2f} MB", ""]
+                     f"O {ent['o_bytes'] / 1e6:.2f} MB (`{ent.get('kernel', '')}`)", ""]
+            if len(ent.get("kernels", {})) > 1:
+                text += [f"- `{k}`: read {v.get('hbm_read_bytes_per_launch', 0) / 1e6:.2f} MB, written "
+                         f"{v.get('hbm_write_bytes_per_launch', 0) / 1e6:.2f} MB" for k, v in ent["kernels"].items()]
+                text += [""]
             text += ["```"] + ent.get("commands", []) + ["```", ""]
         with open(os.path.join(ROOT, "profiles", stem + ".md"), "w") as f:
             f.write("\n".join(text))
@@ -497,9 +504,15 @@ def ingest_counters(pmc_dir: str, calib_bytes: int):
             v = per_dispatch(f"{counter}_{name}", counter, lambda k: "sdpa_dev" in k)
             if not v:
                 continue
+            f = out["calibration"][counter]["factor"] or 1.0
+            # every kernel of the route (a pre-pass, a combine) per launch; the totals below are
+            # the dominant kernel's, the one with the most traffic
+            for kk in sorted(set(k for k, _ in v)):
+                xk = [x for (k2, _), x in v.items() if k2 == kk]
+                ent.setdefault("kernels", {}).setdefault(_short(kk), {})[f"hbm_{key}_bytes_per_launch"] = \
+                    sum(xk) / len(xk) * 1024.0 * f
             kern = max(set(k for k, _ in v), key=lambda kk: sum(x for (k2, _), x in v.items() if k2 == kk))
             xs = [x for (k, _), x in v.items() if k == kern]
-            f = out["calibration"][counter]["factor"] or 1.0
             ent["kernel"] = _short(kern)
             ent[f"{key}_kib_per_dispatch"] = sum(xs) / len(xs)
             ent[f"hbm_{key}_bytes_per_launch"] = sum(xs) / len(xs) * 1024.0 * f

@@ -382,10 +382,13 @@ std::string route_string(int batch, int q_len, int kv_len, int hq, int hkv, int 
         const FullPlan fp = full_plan(ks, variant, batch, q_len, hq, hkv);
         const auto& t = *fp.cfg;
         const FullGrid fg = fp.grid;
+        // a boolean mask with the workspace sdpa_workspace_size() names: lane words
+        // built by a pre-pass launch, then the kernel
+        const bool words = mk == SDPA_MASK_BOOLEAN && ks->full_bits && !fp.small;
         std::snprintf(buf, sizeof buf,
-                      "full %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d tile=%dx%d waves=%dx%d lds=%d workgroups=%ld%s",
+                      "full %s d%s %s B=%d Lq=%d Lk=%d Hq=%d Hkv=%d tile=%dx%d waves=%dx%d lds=%d workgroups=%ld%s%s",
                       dtype_name(dt), dn, mask_name(mk), batch, q_len, kv_len, hq, hkv, t.cols, t.bn, t.wm, t.wd,
-                      t.lds, fg.items, fg.pairs ? " causal-pairs" : "");
+                      t.lds, fg.items, fg.pairs ? " causal-pairs" : "", words ? " lane-words+prepass" : "");
     } else {
         const auto& t = ks->dec_cfg;
         const FusedPlan f = fused_plan(ks, batch, q_len, kv_len, hq, hkv, 0, kernel_variant(mk, SDPA_BF16));
@@ -838,7 +841,9 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
             a.Lk = kv_len;
             a.RB = rbn;
             a.KT = ktn;
-            a.vec = p.mask_vec;
+            // 16-byte loads: key stride 1 and every row start 16-byte aligned
+            const uintptr_t mp = (uintptr_t)p.mask;
+            a.vec = p.ms[3] == 1 && mp % 16 == 0 && p.ms[0] % 16 == 0 && p.ms[1] % 16 == 0 && p.ms[2] % 16 == 0;
             const int64_t units = (int64_t)bm * hm * rbn * ktn;
             hipLaunchKernelGGL(sdpa_dev::mask_bits_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, a);
             if ((st = hip_status(hipGetLastError())) != SDPA_OK) return reject(st);

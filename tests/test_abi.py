@@ -100,6 +100,11 @@ def test_describe_route(lib):
     s = sdpa.describe_route(1, 8192, 8192, 16, 16, 72, 2, "causal")
     assert s.startswith("full bf16 d72 causal")
     assert sdpa.describe_route(1, 9, 9, 8, 4, 65, 2).startswith("unsupported")
+    # a boolean mask on the 16-bit head-dim <= 128 kernel: lane words built by a pre-pass launch
+    assert sdpa.describe_route(1, 8192, 8192, 16, 16, 72, 2, "boolean").endswith(" lane-words+prepass")
+    assert "lane-words" not in sdpa.describe_route(1, 8192, 8192, 16, 16, 72, 2, "none")
+    assert "lane-words" not in sdpa.describe_route(1, 4096, 4096, 32, 4, 512, 2, "boolean")
+    assert "lane-words" not in sdpa.describe_route(1, 100, 100, 8, 2, 64, 0, "boolean")
 
 
 def test_workspace_size(lib):

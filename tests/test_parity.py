@@ -398,7 +398,10 @@ def test_decode_forced_single_split(gpu_lib, monkeypatch, D, dv, mask_kind):
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("D,B,Hq,Hkv,Lq,Lk,shape", [(72, 1, 4, 2, 300, 333, "qk"), (64, 2, 4, 4, 129, 65, "full"),
                                                     (128, 1, 8, 2, 100, 1000, "qk"), (96, 2, 2, 1, 40, 4100, "full"),
-                                                    (80, 1, 3, 1, 1030, 300, "qk")])
+                                                    (80, 1, 3, 1, 1030, 300, "qk"),
+                                                    # 16-byte aligned mask rows (the pre-pass's vector loads),
+                                                    # a ragged last key tile, a per-head mask
+                                                    (72, 1, 4, 2, 300, 336, "qk"), (64, 2, 4, 4, 130, 1024, "full")])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_boolean_lane_masks_equal_the_byte_path(gpu_lib, D, B, Hq, Hkv, Lq, Lk, shape, dtype):
     c = si.make_case(B, Hq, Hkv, Lq, Lk, D, dtype=dtype, mask_kind="boolean", mask_shape=shape, mask_p=0.3,
