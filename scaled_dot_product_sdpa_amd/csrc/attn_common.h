@@ -212,19 +212,24 @@ __device__ __forceinline__ void buffer_load16_lds_so(__amdgpu_buffer_rsrc_t r, v
 // the LDS base, with the one wait state the DMA needs after writing it.
 // Compiler-issued vector loads newer than these get waits counted without
 // them, which only makes those waits stricter.
-__device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
+// LDS byte address of a pointer into a __shared__ array (the M0 value the
+// DMA wants).  Taken once from the array itself, where the compiler knows
+// the address space; offsets are then plain integer adds.
+__device__ __forceinline__ uint32_t lds_address(const void* shared_array) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)shared_array;
+}
+__device__ __forceinline__ void dma16_lds(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory");
 #endif
 }
-__device__ __forceinline__ void dma16_lds_so(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ void dma16_lds_so(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff,
+                                             uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r),
-                 "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(m0)
+                 "s"(__builtin_amdgcn_readfirstlane(soff)), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                  : "memory");
 #endif
 }
