@@ -158,11 +158,21 @@ def graph_time(step, steps: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
+MARKER = "spin_kernel"  # torch.cuda._sleep's kernel: starts each measured workload in a trace
+
+
+def mark_workload():
+    """A few-microsecond spin kernel that opens each workload's stretch of a kernel trace."""
+    import torch
+    torch.cuda._sleep(1000)
+
+
 def measure(name: str, steps: int, warmup: int, eager: bool = False) -> dict:
     import torch
     import scaled_dot_product_sdpa_amd as sdpa
     import sdpa_inputs as si
 
+    mark_workload()
     c = make_case(name)
     amount, unit = work(c)
     decode = unit == "bytes"
@@ -221,6 +231,7 @@ def ceiling(nbytes: int, steps: int) -> dict:
     """The library's plain streaming read of nbytes, cold, timed like a decode step."""
     import torch
     import scaled_dot_product_sdpa_amd as sdpa
+    mark_workload()
     nrep = max(2, -(-COLD_BYTES // nbytes))
     bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nrep)]
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -335,16 +346,19 @@ def trace_runs(trace_csv: str, steps: int):
     of each workload's timed graph replay (the last `steps` launches of each kernel in that
     workload's stretch of the trace), their average duration and the average start-to-start period.
 
-    Workloads are measured one after another, separated by host work (input generation) of
-    milliseconds; the stretches are split at gaps of more than 5 ms and named in the bench's
-    order: the primary workload, the others in WORKLOADS order, then the streaming-read ceiling."""
+    Workloads are measured one after another, each opened by a marker kernel (mark_workload);
+    the stretches between markers are named in the bench's order: the primary workload, the
+    others in WORKLOADS order, then the streaming-read ceiling.  (A trace without markers is
+    split at gaps of more than 5 ms instead.)"""
     rows = list(csv.DictReader(open(trace_csv)))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    marked = any(MARKER in r["Kernel_Name"] for r in rows)
     segs, cur, prev = [], [], None
     for r in rows:
         s0, e0 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
-        if prev is not None and s0 - prev > 5_000_000:
-            segs.append(cur)
+        if (MARKER in r["Kernel_Name"]) if marked else (prev is not None and s0 - prev > 5_000_000):
+            if cur:
+                segs.append(cur)
             cur = []
         cur.append(r)
         prev = e0
