@@ -750,6 +750,7 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     p.scale_nonneg = scale >= 0.f;
     p.window = window;
     p.kbase = 0;
+    size_t rope_bytes = 0;
     if (q_rope && q_rope->rotary_dim != 0) {
         const int r = q_rope->rotary_dim;
         if (r < 0 || r % 2 != 0 || r > head_dim) return reject(SDPA_EUNSUPPORTED);
@@ -758,6 +759,7 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         if (((uintptr_t)q_rope->cos) % 16 != 0 || ((uintptr_t)q_rope->sin) % 16 != 0) return reject(SDPA_EUNSUPPORTED);
         const size_t tb = (size_t)q_rope->n_pos * (size_t)(r / 2) * sizeof(float);
         if (overlaps(out, oq, q_rope->cos, tb) || overlaps(out, oq, q_rope->sin, tb)) return reject(SDPA_EINVAL);
+        rope_bytes = tb;
         p.rope_dim = r;
         p.rope_pos0 = q_pos0;
         p.rope_cos = q_rope->cos;
@@ -799,6 +801,14 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         }
     };
 
+    // bytes a kernel writes in the workspace must not be an operand any kernel reads
+    // or the output it writes
+    auto ws_overlaps = [&](const void* w, size_t n) {
+        return overlaps(out, oq, w, n) || overlaps(q, sq, w, n) || overlaps(k, sk, w, n) || overlaps(v, sv, w, n) ||
+               (p.mask && overlaps(p.mask, (size_t)p.mask_span, w, n)) ||
+               (rope_bytes && (overlaps(p.rope_cos, rope_bytes, w, n) || overlaps(p.rope_sin, rope_bytes, w, n)));
+    };
+
     if (kern == SDPA_KERNEL_FULL) {
         const FullPlan fp = full_plan(ks, mk, batch, q_len, n_q_heads, n_kv_heads);
         p.pairs = fp.grid.pairs;
@@ -818,10 +828,7 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
                           workspace_bytes >= kCounterBytes + bits_need && ((uintptr_t)workspace) % 256 == 0 &&
                           bits_need < ((size_t)1 << 34);
         char* const bits_at = reinterpret_cast<char*>(workspace) + kCounterBytes;
-        if (bits && (overlaps(out, oq, bits_at, bits_need) || overlaps(q, sq, bits_at, bits_need) ||
-                     overlaps(k, sk, bits_at, bits_need) || overlaps(v, sv, bits_at, bits_need) ||
-                     overlaps(p.mask, (size_t)p.mask_span, bits_at, bits_need)))
-            return reject(SDPA_EINVAL);
+        if (bits && ws_overlaps(bits_at, bits_need)) return reject(SDPA_EINVAL);
         const launch_fn f = bits         ? (rope_k ? ks->full_bits_rope : ks->full_bits)
                             : fp.small   ? (rope_k ? ks->full_small_rope[mk] : ks->full_small[mk])
                             : strided    ? (rope_k ? ks->full_strided_rope[mk] : ks->full_strided[mk])
@@ -876,10 +883,7 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
         const size_t need = fused_ws_bytes(fpl, v_head_dim);
         if (need && (!workspace || workspace_bytes < need)) return reject(SDPA_EWORKSPACE);
         if (need && ((uintptr_t)workspace) % 256 != 0) return reject(SDPA_EINVAL);
-        if (need && (overlaps(out, oq, workspace, need) || overlaps(q, sq, workspace, need) ||
-                     overlaps(k, sk, workspace, need) || overlaps(v, sv, workspace, need) ||
-                     (p.mask && overlaps(p.mask, (size_t)p.mask_span, workspace, need))))
-            return reject(SDPA_EINVAL);
+        if (need && ws_overlaps(workspace, need)) return reject(SDPA_EINVAL);
         const size_t slots = (size_t)fpl.groups * fpl.splits * fpl.rv;
         p.ws_o = reinterpret_cast<float*>(workspace);
         p.ws_ml = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kCounterBytes +
@@ -911,10 +915,7 @@ int forward_impl(const void* q, sdpa_strides q_st, const void* k, sdpa_strides k
     const size_t need = decode_ws_bytes(batch, q_len, n_q_heads, v_head_dim, plan.splits, dtype);
     if (need && (!workspace || workspace_bytes < need)) return reject(SDPA_EWORKSPACE);
     if (need && ((uintptr_t)workspace) % 256 != 0) return reject(SDPA_EINVAL);
-    if (need && (overlaps(out, oq, workspace, need) || overlaps(q, sq, workspace, need) ||
-                 overlaps(k, sk, workspace, need) || overlaps(v, sv, workspace, need) ||
-                 (p.mask && overlaps(p.mask, (size_t)p.mask_span, workspace, need))))
-        return reject(SDPA_EINVAL);
+    if (need && ws_overlaps(workspace, need)) return reject(SDPA_EINVAL);
     if ((long)n_kv_heads * plan.col_groups > kMaxGridYZ) return reject(SDPA_EUNSUPPORTED);
     const size_t rows = (size_t)batch * n_q_heads * q_len;
     p.ws_o = need ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + kCounterBytes) : nullptr;

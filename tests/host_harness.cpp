@@ -290,6 +290,18 @@ void check_overlaps() {
                                 100, 8, 8, 64, SDPA_BF16, 0.125f, SDPA_MASK_BOOLEAN, (const void*)(kM + 64),
                                 sdpa_strides{0, 0, 100, 1}, SDPA_U8, nullptr, 0, nullptr);
     CHECK(st == SDPA_EINVAL, "out over the mask: %d", st);
+    // a workspace over the rotary tables (read by the kernels that write the workspace)
+    const sdpa_strides q2 = bhld(32, 1, 256), k2 = bhld(8, 4096, 256);
+    const sdpa_rope_table tab{64, (const float*)(kW + 4096), (const float*)(kM + (1u << 20)), 8192};
+    const int st2 = sdpa_forward_ex((const void*)kQ, q2, (const void*)kK, k2, (const void*)kV, k2, (void*)kO, q2, 1, 1,
+                                    4096, 32, 8, 256, 256, SDPA_BF16, 0.0625f, SDPA_MASK_NONE, nullptr,
+                                    sdpa_strides{0, 0, 0, 0}, SDPA_BF16, 0, &tab, 4095, (void*)kW, ws, nullptr);
+    CHECK(st2 == SDPA_EINVAL, "workspace over the rope tables: %d", st2);
+    const sdpa_rope_table tab_ok{64, (const float*)(kM + (2u << 20)), (const float*)(kM + (1u << 20)), 8192};
+    const int st3 = sdpa_forward_ex((const void*)kQ, q2, (const void*)kK, k2, (const void*)kV, k2, (void*)kO, q2, 1, 1,
+                                    4096, 32, 8, 256, 256, SDPA_BF16, 0.0625f, SDPA_MASK_NONE, nullptr,
+                                    sdpa_strides{0, 0, 0, 0}, SDPA_BF16, 0, &tab_ok, 4095, (void*)kW, ws, nullptr);
+    CHECK(st3 == SDPA_OK, "tables apart from the workspace: %d", st3);
 }
 
 void concurrent_queries() {
