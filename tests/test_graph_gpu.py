@@ -46,8 +46,12 @@ CASES = [
     ("decode-f32", dict(B=2, Hq=4, Hkv=4, Lq=3, Lk=82, D=64, dtype="f32"), "vector", ""),
     ("prefill-d72-causal-pairs", dict(B=1, Hq=16, Hkv=16, Lq=4096, Lk=4096, D=72, mask_kind="causal",
                                       layout="blhd"), "full", "causal-pairs"),
+    # boolean masks: the lane-word pre-pass and the kernel both captured; the words sit in the
+    # clobbered part of the workspace and are rebuilt by every replay
     ("prefill-d128-boolean", dict(B=1, Hq=4, Hkv=2, Lq=300, Lk=333, D=128, mask_kind="boolean",
-                                  mask_shape="qk"), "full", ""),
+                                  mask_shape="qk"), "full", "lane-words+prepass"),
+    ("prefill-d72-boolean-aligned", dict(B=1, Hq=8, Hkv=2, Lq=256, Lk=320, D=72, mask_kind="boolean",
+                                         mask_shape="full"), "full", "lane-words+prepass"),
     # (a launch with dynamic LDS padding: mask tensors below D = 128)
     ("prefill-d72-additive", dict(B=1, Hq=4, Hkv=2, Lq=300, Lk=332, D=72, mask_kind="additive",
                                   mask_shape="qk"), "full", ""),

@@ -43,6 +43,9 @@ CASES = [
     ("decode sliding, smaller", dict(B=2, Hq=16, Hkv=4, Lq=3, Lk=500, D=64, mask_kind="sliding", window=40),
      "vector-fused"),
     ("prefill (no scratch)", dict(B=1, Hq=4, Hkv=2, Lq=200, Lk=200, D=72, mask_kind="causal"), "full"),
+    ("prefill boolean, lane words in the scratch", dict(B=1, Hq=4, Hkv=2, Lq=300, Lk=320, D=72,
+                                                      mask_kind="boolean", mask_shape="qk"), "lane-words"),
+    ("decode after it, smaller", dict(B=1, Hq=32, Hkv=8, Lq=1, Lk=1000, D=128, mask_kind="none"), "vector-fused"),
 ]
 
 
