@@ -48,6 +48,11 @@ struct PfCfg {
     static constexpr int NDB = (D + 31) / 32;         // 32-column O^T blocks
     static constexpr int NKB = BN / 32;               // 32-key score blocks per tile
     static constexpr bool ONES = (D % 32) != 0;
+    // REM: the last O^T columns (the D % 32 real ones, then the row-sum column)
+    // fit 16 columns, which take v_mfma_f32_16x16x32 products instead of a third
+    // of a 32-column block (head dim 72: 80 O^T columns, not 96)
+    static constexpr bool REM = ONES && (D % 32) < 16;
+    static constexpr int NDF = REM ? D / 32 : NDB;    // 32-column O^T blocks on 32x32x16 products
     static constexpr int LA = 3;                      // operand reads in flight ahead of the MFMAs
     static constexpr bool PAIRS = true;               // causal: two row tiles per workgroup (see the kernel)
     static constexpr int SLOTS = BN * RC;             // 16-byte slots per tile
@@ -264,9 +269,12 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         };
 
         float m_run = NEG_INF, l_run = 0.f;
-        f32x16_t oacc[C::NDB];
+        f32x16_t oacc[C::NDF];
     #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16_t{};
+        for (int db = 0; db < C::NDF; ++db) oacc[db] = f32x16_t{};
+        // REM: O^T columns 32 NDF .. + 15 of query rows qmin + (lane % 16) (orem[0]) and
+        // qmin + 16 + (lane % 16) (orem[1]), head-dim columns 32 NDF + 4 (lane / 16) .. + 3
+        f32x4_t orem[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
         const float c_scale = p.scale_log2 == 0.f ? 1.f : __builtin_fabsf(p.scale_log2);
 
         // per-lane LDS read offsets (loop invariant; the swizzle depends on the
@@ -276,15 +284,20 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         // 32 db + 16 (grp & 1) + 4 j4 .. + 3, i.e. chunk 4 db + 2 (grp & 1) + j4 / 2, half j4 & 1.
         const int grp = lane >> 4, s16 = lane & 15;
         const int e4 = s16 >> 2, j4 = s16 & 3;
-        uint32_t koff[C::NCH], voff[2][C::NDB];
+        uint32_t koff[C::NCH], voff[2][C::NDF], voffr[2];
     #pragma unroll
         for (int ch = 0; ch < C::NCH; ++ch) koff[ch] = (uint32_t)(col * C::ROWB + ((2 * ch + hh) ^ C::sw(col)) * 16);
     #pragma unroll
         for (int w = 0; w < 2; ++w) {
             const int kr = 4 * (grp >> 1) + e4 + 8 * w;
     #pragma unroll
-            for (int db = 0; db < C::NDB; ++db)
+            for (int db = 0; db < C::NDF; ++db)
                 voff[w][db] = (uint32_t)(kr * C::ROWB + ((4 * db + 2 * (grp & 1) + (j4 >> 1)) ^ C::sw(kr)) * 16 + 8 * (j4 & 1));
+            // REM (16x16x32 A operand: head-dim column 32 NDF + lane % 16, eight keys per
+            // 16-lane group): group g reads keys 4 (g / 2) + 16 (g % 2) + {0..3, 8..11} of a
+            // 32-key block, the key order the swapped P registers hold (below)
+            const int krr = 4 * (grp >> 1) + 16 * (grp & 1) + e4 + 8 * w;
+            voffr[w] = (uint32_t)(krr * C::ROWB + (4 * C::NDF + (j4 >> 1)) * 16 + 8 * (j4 & 1));
         }
 
         // S^T of one tile from LDS stage `stage`; operand reads run LA products
@@ -319,9 +332,14 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
                 l_run *= alpha;
                 asm volatile("");  // keep this a branch, not a select on every tile
     #pragma unroll
-                for (int db = 0; db < C::NDB; ++db)
+                for (int db = 0; db < C::NDF; ++db)
     #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                if constexpr (C::REM) {  // rows lane % 16 and 16 + lane % 16: their lanes' factors
+                    const f32x2_t a2 = pair16(alpha);
+                    orem[0] *= a2[0];
+                    orem[1] *= a2[1];
+                }
             }
             const float muse = (m_run == NEG_INF) ? 0.f : m_run;
             float lsum = 0.f;
@@ -344,13 +362,20 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
     #pragma unroll
                     for (int w = 0; w < 4; ++w)
                         bf[kb][pc][w] = TR::pack(sacc[kb][8 * pc + 2 * w], sacc[kb][8 * pc + 2 * w + 1]);
-            // products (kb, pc, db), db fastest; V^T operand reads run LA products ahead
-            constexpr int N = C::NKB * 2 * C::NDB, LAV = C::LA;
+            // operand reads (kb, j): j < 2 NDF the 32-column products (pc, db), db fastest;
+            // j = 2 NDF (REM) the 16-column block of the 32 keys.  Reads run LA ahead.
+            constexpr int E = 2 * C::NDF + (C::REM ? 1 : 0), N = C::NKB * E, LAV = C::LA;
             auto rd = [&](int i) {
-                const int db = i % C::NDB, pc = (i / C::NDB) & 1, kb = i / (2 * C::NDB);
-                const char* vk = vt_lds + (kb * 32 + 16 * pc) * C::ROWB;
-                const u32x2_t y0 = lds_read_tr16(vk + voff[0][db]);
-                const u32x2_t y1 = lds_read_tr16(vk + voff[1][db]);
+                const int kb = i / E, j = i % E;
+                const char* vk = vt_lds + kb * 32 * C::ROWB;
+                if (C::REM && j == 2 * C::NDF) {
+                    const u32x2_t y0 = lds_read_tr16(vk + voffr[0]);
+                    const u32x2_t y1 = lds_read_tr16(vk + voffr[1]);
+                    return u32x4_t{y0[0], y0[1], y1[0], y1[1]};
+                }
+                const int db = j % C::NDF, pc = j / C::NDF;
+                const u32x2_t y0 = lds_read_tr16(vk + 16 * pc * C::ROWB + voff[0][db]);
+                const u32x2_t y1 = lds_read_tr16(vk + 16 * pc * C::ROWB + voff[1][db]);
                 return u32x4_t{y0[0], y0[1], y1[0], y1[1]};
             };
             u32x4_t ring[LAV];
@@ -361,8 +386,27 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
                 const u32x4_t a = ring[i % LAV];
                 if (i + LAV < N) ring[i % LAV] = rd(i + LAV);
                 __builtin_amdgcn_sched_barrier(0);
-                const int db = i % C::NDB, pc = (i / C::NDB) & 1, kb = i / (2 * C::NDB);
-                oacc[db] = TR::mma(a, bf[kb][pc], oacc[db]);
+                const int kb = i / E, j = i % E;
+                if (C::REM && j == 2 * C::NDF) {
+                    // the 16x16x32 B operand: query rows lane % 16 (first product) and
+                    // 16 + lane % 16 (second), eight keys per 16-lane group.  Swapping the
+                    // odd 16-lane rows of the pc = 0 registers with the even rows of the
+                    // pc = 1 registers gathers them: group g then holds keys
+                    // 4 (g / 2) + 16 (g % 2) + {0..3, 8..11} in both registers, for the
+                    // first and the second 16 rows.  Both 32-column products of this
+                    // block have read these registers already.
+    #pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const auto sw2 = __builtin_amdgcn_permlane16_swap(bf[kb][0][w], bf[kb][1][w], false, false);
+                        bf[kb][0][w] = sw2[0];
+                        bf[kb][1][w] = sw2[1];
+                    }
+                    orem[0] = Mma16<TR>::mma(a, bf[kb][0], orem[0]);
+                    orem[1] = Mma16<TR>::mma(a, bf[kb][1], orem[1]);
+                } else {
+                    const int db = j % C::NDF, pc = j / C::NDF;
+                    oacc[db] = TR::mma(a, bf[kb][pc], oacc[db]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -470,7 +514,15 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
 
         // ---- epilogue ----
         float lsum_row;
-        if constexpr (C::ONES) {
+        if constexpr (C::REM) {
+            // the row-sum column D is element rr % 4 of lane group rr / 4 (rr = D % 32)
+            // in orem[0] for rows 0..15 and orem[1] for rows 16..31 of the wave
+            constexpr int rr = D % 32, GR = rr / 4, ER = rr % 4;
+            const int src = (16 * GR + (col & 15)) * 4;
+            const float xl = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(orem[0][ER])));
+            const float xh = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(orem[1][ER])));
+            lsum_row = col < 16 ? xl : xh;
+        } else if constexpr (C::ONES) {
             constexpr int rr = D % 32;
             constexpr int RL = 4 * (rr / 8) + (rr % 4), HL = (rr % 8) / 4, DBL = D / 32;
             const float x = oacc[DBL][RL];
@@ -479,12 +531,25 @@ __global__ __launch_bounds__(C::NT, C::OCC) void prefill_kernel(const Params p) 
         } else {
             lsum_row = sum_x32(l_run);
         }
+        const float inv = lsum_row > 0.f ? 1.f / lsum_row : 0.f;
+        if constexpr (C::REM) {  // columns 32 NDF + 4 (lane / 16) .. + 3 of rows lane % 16 and 16 + lane % 16
+            const f32x2_t inv2 = pair16(inv);
+            const int d0 = 32 * C::NDF + 4 * (lane >> 4);
+    #pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int qr = qmin + 16 * h + (lane & 15);
+                if (qr < p.Lq && d0 < D) {
+                    char* orow = reinterpret_cast<char*>(p.o) +
+                                 ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qr * p.os[2]) * 2;
+                    TR::store4(orow + d0 * 2, orem[h] * inv2[h]);
+                }
+            }
+        }
         if (rv) {
-            const float inv = lsum_row > 0.f ? 1.f / lsum_row : 0.f;
             char* orow = reinterpret_cast<char*>(p.o) +
                          ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2]) * 2;
     #pragma unroll
-            for (int db = 0; db < C::NDB; ++db)
+            for (int db = 0; db < C::NDF; ++db)
     #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
                     const int d0 = 32 * db + 8 * a4 + 4 * hh;
