@@ -246,6 +246,131 @@ def ceiling(nbytes: int, steps: int) -> dict:
 
 
 # ---------------------------------------------------------------- CPU baseline
+TRACE_LIB = os.path.join(ROOT, "scaled_dot_product_sdpa_amd", "libsdpa_trace.so")
+TRACE_BUILD = ("python3 -m scaled_dot_product_sdpa_amd.build -D SDPA_TRACE_DECODE=1 "
+               "--out scaled_dot_product_sdpa_amd/libsdpa_trace.so --build-dir scaled_dot_product_sdpa_amd/_build/trace")
+TRACE_WORDS = 14
+TRACE_STAGES = (  # (record word, what the workgroup has done by then, last workgroups only)
+    (0, "started (arguments loaded)", False),
+    (1, "wave 0: first 16-key block in registers (its S^T products done)", False),
+    (3, "every wave: its keys done (after the merge barrier)", False),
+    (8, "wave partials in LDS (barrier)", False),
+    (9, "partial stores issued", False),
+    (4, "partial stored in L2 (s_waitcnt vmcnt(0) + barrier)", False),
+    (5, "arrival add returned", False),
+    (10, "last workgroup of a group: merge weights in LDS", True),
+    (11, "last workgroup of a group: weighted partial sums in LDS", True),
+    (6, "last workgroup of a group: output stored", True),
+    (12, "(a second clock read right after 'every wave: its keys done')", False),
+    (13, "(a second clock read right after 'partial stores issued')", False),
+)
+
+
+def timeline(name: str, calls: int, warmup: int, command: str) -> str:
+    """In-kernel timeline of the single-launch decode kernel, from the timeline build of the library
+    (libsdpa_trace.so): every workgroup records the constant 100 MHz clock at the stages of
+    TRACE_STAGES.  Each call runs on an idle GPU (a synchronize before and after); times are relative
+    to the first workgroup's start in the same call.  Returns a markdown summary."""
+    import re
+    import statistics as stt
+    import numpy as np
+    import torch
+    import scaled_dot_product_sdpa_amd as sdpa
+    import sdpa_inputs as si
+
+    c = make_case(name)
+    d = c.dims
+    dv = int(c.v.shape[3])
+    kv_bytes = 2 * c.k.numel() * c.k.element_size()
+    nrep = max(2, -(-COLD_BYTES // kv_bytes))
+    reps = [si.to_device(c) for _ in range(nrep)]
+    q0 = reps[0][0]
+    out = torch.empty(q0.shape[:3] + (dv,), dtype=q0.dtype, device="cuda")
+    ws_bytes = sdpa.workspace_size(d["batch"], d["q_len"], d["kv_len"], d["n_q_heads"], d["n_kv_heads"],
+                                   d["head_dim"], q0.dtype, v_head_dim=dv)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    route = sdpa.describe_route(d["batch"], d["q_len"], d["kv_len"], d["n_q_heads"], d["n_kv_heads"],
+                                d["head_dim"], q0.dtype, c.mask_kind, v_head_dim=dv)
+    if not route.startswith("vector-fused"):
+        raise SystemExit(f"{name}: not the single-launch decode kernel ({route})")
+    G, S = (int(re.search(k + r"=(\d+)", route).group(1)) for k in ("groups", "splits"))
+    rv = min(16, d["n_q_heads"] // d["n_kv_heads"] * d["q_len"])
+    a256 = lambda x: (x + 255) // 256 * 256
+    slots = G * S * rv
+    off = 32768 + a256(slots * dv * 4) + a256(slots * 8)
+    nwg = G * S
+    rb = TRACE_WORDS * 8
+    if S < 2 or off + nwg * rb > ws_bytes:
+        raise SystemExit(f"{name}: no timeline records in this library's workspace (is it the timeline build?)")
+    recs, durs = [], []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(warmup + calls):
+        q, k, v, m = reps[i % nrep]
+        ws[off:off + nwg * rb].zero_()
+        torch.cuda.synchronize()
+        e0.record()
+        sdpa.forward(q, k, v, scale=c.scale, mask=m, mask_kind=c.mask_kind, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= warmup:
+            r = ws[off:off + nwg * rb].view(torch.int64).view(nwg, TRACE_WORDS).cpu().numpy().copy()
+            if (r[:, 0] == 0).any() or (r[:, 5] == 0).any():
+                raise SystemExit("incomplete timeline records (a group recomputed off its XCD?)")
+            recs.append(r)
+            durs.append(e0.elapsed_time(e1) * 1000)
+    us = 0.01  # microseconds per tick of the 100 MHz clock
+    per = {k: ([], []) for k, _, _ in TRACE_STAGES}
+    segs = {n: [] for n in ("load", "keys", "store", "arrive", "merge", "span")}
+    crit = {k: [] for k, _, _ in TRACE_STAGES}
+    crit_keys = []
+    for r in recs:
+        t0 = r[:, 0].min()
+        t = (np.where(r > 0, r, t0) - t0) * us
+        last = ((r[:, 7] >> 4) & 1) == 1
+        grp = r[:, 7] >> 16
+        for k, _, lo in TRACE_STAGES:
+            col = t[last, k] if lo else t[:, k]
+            per[k][0].append(float(np.median(col)))
+            per[k][1].append(float(col.max()))
+        segs["load"].append(float(np.median(t[:, 1] - t[:, 0])))
+        segs["keys"].append(float(np.median(t[:, 3] - t[:, 1])))
+        segs["store"].append(float(np.median(t[:, 4] - t[:, 3])))
+        segs["arrive"].append(float(np.median(t[:, 5] - t[:, 4])))
+        segs["merge"].append(float(np.median(t[last, 6] - t[last, 5])))
+        segs["span"].append(float(t[last, 6].max()))
+        w = int(np.argmax(np.where(last, t[:, 6], -1)))  # the workgroup that finished the call
+        for k, _, _ in TRACE_STAGES:
+            crit[k].append(float(t[w, k]))
+        crit_keys.append(float(t[grp == grp[w], 3].max()))
+    med = stt.median
+    lines = [f"# Single-launch decode: in-kernel timeline, {name}", "",
+             f"Route: `{route}`.", "",
+             "Built and run from the repository root (the timeline build is the library compiled with",
+             "`SDPA_TRACE_DECODE=1`: each workgroup records the 100 MHz real-time clock at the stages below",
+             "into the workspace; the product build has none of it):", "",
+             "```", TRACE_BUILD, command, "```", "",
+             f"{calls} calls on cold K/V replicas, each on an idle GPU; times in µs from the first workgroup's",
+             "start in the same call, medians over the calls; 10 ns resolution.",
+             f"HIP-event time of one isolated call (host launch included): {med(durs):.2f} µs.", "",
+             "| stage | median workgroup | last workgroup |", "|---|---|---|"]
+    for k, label, _ in TRACE_STAGES:
+        lines.append(f"| {label} | {med(per[k][0]):.2f} | {med(per[k][1]):.2f} |")
+    lines += ["", "Per-workgroup segments (median workgroup, medians over the calls):", "",
+              "| segment | µs |", "|---|---|",
+              f"| start → first block in registers (load latency under the full stream) | {med(segs['load']):.2f} |",
+              f"| first block → every wave's keys done | {med(segs['keys']):.2f} |",
+              f"| keys done → partial stored in L2 (wave merge, stores, their completion) | {med(segs['store']):.2f} |",
+              f"| partial stored → arrival add returned | {med(segs['arrive']):.2f} |",
+              f"| arrival → output stored (last workgroups: the merge of {S} partials) | {med(segs['merge']):.2f} |",
+              f"| first start → last output stored (in-kernel span) | {med(segs['span']):.2f} |",
+              "", "Critical path (the workgroup that stored the call's last output, medians over the calls):", "",
+              "| stage | µs |", "|---|---|"]
+    for k, label, _ in TRACE_STAGES:
+        lines.append(f"| {label} | {med(crit[k]):.2f} |")
+    lines.append(f"| latest split of that group done with its keys | {med(crit_keys):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def _oracle_task(args):
     """One (batch, query head) of a workload through the float64 oracle, single-threaded BLAS."""
     import numpy as np
@@ -558,6 +683,8 @@ def main():
                     help="only run --steps device-to-device copies of MIB MiB (calibrates rocprofv3 byte counters)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("CSV", "COMMAND"),
                     help="print a markdown summary of a rocprofv3 kernel trace (no GPU needed)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="in-kernel timeline of --workload's single-launch decode (needs libsdpa_trace.so)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("DIR", "COPY_MIB"),
                     help="write profiles/counters.json from rocprofv3 --pmc output (no GPU needed)")
     a = ap.parse_args()
@@ -583,6 +710,14 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     torch.cuda.set_device(0)
+    if a.timeline:
+        from scaled_dot_product_sdpa_amd import _lib
+        if not os.path.exists(TRACE_LIB):
+            raise SystemExit(f"{TRACE_LIB} not built: {TRACE_BUILD}")
+        _lib.load(TRACE_LIB)
+        cmd = "python3 bench.py --timeline" + (f" --workload {a.workload}" if a.workload != PRIMARY else "")
+        print(timeline(a.workload, a.steps if a.steps != 200 else 50, 5, cmd), flush=True)
+        return
     sdpa.load()
 
     if a.profile_copy:

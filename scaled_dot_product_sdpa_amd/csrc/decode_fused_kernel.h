@@ -72,7 +72,11 @@ struct DfCfg {
     static constexpr int VSLOTS = 16 * VCHP;               // 16-byte slots of one V block (incl. pad chunks)
     static constexpr int VU = (VSLOTS + 63) / 64;          // V load slots per lane per block
     static constexpr int LDS_V = NW * 16 * PITCH * 16;     // one V block per wave
-    static constexpr int LDS_M = NW * 16 * DVP * 4 + 2 * NW * 16 * 4;  // per-wave O^T + (m, l) for the merge
+    // per-wave O^T rows for the merge, padded to 16 banks past a multiple of 64: the
+    // 4 x 4 lanes (row, column quad) of one 16-byte write per row then cover the 64
+    // banks instead of 4-way conflicting on 1 KB rows
+    static constexpr int OP = DVP + (80 - DVP % 64) % 64;
+    static constexpr int LDS_M = NW * 16 * OP * 4 + 2 * NW * 16 * 4;  // per-wave O^T + (m, l) for the merge
     static constexpr int LDS_G = 16 * 32 * 4 + 2 * 16 * (DOW / 4) * 16;  // group merge: weights, half sums
     static constexpr int LDS_W = LDS_V > LDS_M ? (LDS_V > LDS_G ? LDS_V : LDS_G) : (LDS_M > LDS_G ? LDS_M : LDS_G);
     static constexpr int LDS = LDS_W;
@@ -101,6 +105,26 @@ template <> struct Mma16k16<TF16> {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(bitcast<h4_t>(a), bitcast<h4_t>(b), c, 0, 0, 0);
     }
 };
+
+// Timeline build (SDPA_TRACE_DECODE=1, a separate library; off in the product
+// build): each workgroup of a split group records the constant 100 MHz clock at
+// the points below and writes them, 8 x 64 bits, to the workspace after the
+// (m, l) partials (kTraceWords x 8 bytes per workgroup more workspace).
+//   0 entry   1 wave 0's first block in registers   2 wave 0's keys done
+//   3 every wave's keys done   4 partial stored in L2   5 arrival add returned
+//   6 (last workgroup) output stored   7 xcc | last << 4 | split << 8 | group << 16
+//   8 wave partials in LDS   9 partial stores issued   10 (last) weights in LDS
+//   11 (last) weighted sums in LDS   12, 13 a second clock read right after 3 and 9
+//   (the cost of a read)
+#ifndef SDPA_TRACE_DECODE
+#define SDPA_TRACE_DECODE 0
+#endif
+constexpr int kTraceWords = 14;
+__device__ __forceinline__ uint64_t trace_clock() {
+    uint64_t t;
+    asm volatile("s_memrealtime %0\n s_waitcnt lgkmcnt(0)" : "=s"(t)::"memory");
+    return t;
+}
 
 __device__ __forceinline__ uint32_t xcc_id() {
     return (uint32_t)__builtin_amdgcn_s_getreg((20) | (0 << 6) | ((16 - 1) << 11)) & 0xfu;  // HW_REG_XCC_ID[3:0]
@@ -142,6 +166,8 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
 
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g4 = lane >> 4;
+    uint64_t tr[kTraceWords] = {};
+    if constexpr (SDPA_TRACE_DECODE) tr[0] = trace_clock();
 
     // ---- group and split of this workgroup (32-bit: the host keeps nblk * S below 2^31) ----
     const int i = blockIdx.x;
@@ -178,6 +204,20 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
     float* const part_ml = p.ws_ml;
     const int S = fg.splits.d, RV = fg.rv;
     bool direct = S == 1;
+    // timeline build: this workgroup's record, past the (m, l) partials (256-byte aligned)
+    auto trace_store = [&](bool last) __attribute__((always_inline)) {
+        if constexpr (SDPA_TRACE_DECODE) {
+            if (tid == 0 && S > 1) {
+                const size_t slots = (size_t)fg.groups * S * RV;
+                uint64_t* rec = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(part_ml) +
+                                                            (slots * 8 + 255) / 256 * 256) +
+                                (size_t)blockIdx.x * kTraceWords;
+                tr[7] = (uint64_t)xcc_id() | ((uint64_t)last << 4) | ((uint64_t)split << 8) | ((uint64_t)grp << 16);
+#pragma unroll
+                for (int k = 0; k < kTraceWords; ++k) rec[k] = tr[k];
+            }
+        }
+    };
     char* const vlds = work + w * (16 * C::PITCH * 16);
     // transposed-read offsets: lane (g4, e = (lane % 16) / 4, q = lane % 4) names row 4 g4 + e,
     // columns 16 db + 4 q .. + 3
@@ -250,6 +290,12 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
             f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < C::NCH; ++c) sc = Mma16<TR>::mma(kf[c], qf[c], sc);
+            if constexpr (SDPA_TRACE_DECODE) {
+                if (n == 0 && tr[1] == 0) {
+                    asm volatile("" ::"v"(sc[0]) : "memory");  // after this block's products
+                    tr[1] = trace_clock();
+                }
+            }
             const typename MaskRaw<MASK>::type mk = mr;
             // K, V registers consumed: the next block streams during this one's softmax and P V
             if (n + 1 < nmine) issue(n + 1);
@@ -299,21 +345,34 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
             }
         }
         const float l_row = sum_x32(sum_x16(l_run));
+        if constexpr (SDPA_TRACE_DECODE) {
+            asm volatile("" ::"v"(l_row) : "memory");
+            if (tr[2] == 0) tr[2] = trace_clock();
+        }
 
         // ---- merge the waves through LDS: wave w's O^T, m, l of rows < RV ----
         __syncthreads();  // every wave is done with its V block
+        if constexpr (SDPA_TRACE_DECODE) {
+            if (tr[3] == 0) {
+                tr[3] = trace_clock();
+                tr[12] = trace_clock();
+            }
+        }
         float* lo = reinterpret_cast<float*>(work);
-        float* lml = lo + NW * 16 * C::DVP;
+        float* lml = lo + NW * 16 * C::OP;
         if (r < RV) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                *reinterpret_cast<f32x4_t*>(lo + ((w * 16 + r) * C::DVP + 16 * db + 4 * g4)) = oacc[db];
+                *reinterpret_cast<f32x4_t*>(lo + ((w * 16 + r) * C::OP + 16 * db + 4 * g4)) = oacc[db];
             if (g4 == 0) {
                 lml[(w * 16 + r) * 2] = m_run;
                 lml[(w * 16 + r) * 2 + 1] = l_row;
             }
         }
         __syncthreads();
+        if constexpr (SDPA_TRACE_DECODE) {
+            if (tr[8] == 0) tr[8] = trace_clock();
+        }
         // thread -> (row, 4 columns) items of the group's partial
         constexpr int QPR = DOW / 4;  // column quads per row
         const int nitems = RV * QPR;
@@ -329,7 +388,7 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
                 const float mw = lml[(ww * 16 + row) * 2];
                 const float wt = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
                 l = __builtin_fmaf(wt, lml[(ww * 16 + row) * 2 + 1], l);
-                o += wt * *reinterpret_cast<const f32x4_t*>(lo + ((ww * 16 + row) * C::DVP + c4));
+                o += wt * *reinterpret_cast<const f32x4_t*>(lo + ((ww * 16 + row) * C::OP + c4));
             }
             if (direct) {
                 if (row < rows_g) {
@@ -347,10 +406,15 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
             }
         }
         if (direct) return;
+        if constexpr (SDPA_TRACE_DECODE) {
+            tr[9] = trace_clock();
+            tr[13] = trace_clock();
+        }
 
         // ---- arrival: partial stores complete in L2, then one add on the group's word ----
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        if constexpr (SDPA_TRACE_DECODE) tr[4] = trace_clock();
         const uint32_t xc = xcc_id();
         if (tid == 0) {
             const uint32_t add = 1u + (xc << 8) + ((xc * xc) << 18);
@@ -359,7 +423,11 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
         }
         __syncthreads();
         const uint32_t word = s_word;
-        if ((int)(word & 0xffu) != S) return;  // not the last split of the group
+        if constexpr (SDPA_TRACE_DECODE) tr[5] = trace_clock();
+        if ((int)(word & 0xffu) != S) {  // not the last split of the group
+            trace_store(false);
+            return;
+        }
         if (tid == 0)
             __hip_atomic_exchange(&words[grp * kFusedCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool one_xcd = ((word >> 8) & 0x3ffu) == (uint32_t)S * xc && (word >> 18) == (uint32_t)S * xc * xc;
@@ -423,6 +491,7 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
             if (lane < MAXS) wts[rw * MAXS + lane] = (den > 0.f && lane < S) ? wt / den : 0.f;
         }
         __syncthreads();
+        if constexpr (SDPA_TRACE_DECODE) tr[10] = trace_clock();
         for (int u = tid; u < nunits; u += C::NT) {
             if (u != tid) load_unit(u);
             const int it = u % nitems, h = u / nitems;
@@ -439,6 +508,7 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
             ob[h * nitems + it] = o;
         }
         __syncthreads();
+        if constexpr (SDPA_TRACE_DECODE) tr[11] = trace_clock();
         for (int it = tid; it < nitems; it += C::NT) {
             const int row = it / QPR, c4 = (it % QPR) * 4;
             if (row >= rows_g) continue;
@@ -449,6 +519,12 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
             char* dst = reinterpret_cast<char*>(p.o) +
                         ((int64_t)b * p.os[0] + (int64_t)oqh * p.os[1] + (int64_t)oqi * p.os[2] + c4) * 2;
             TR::store4(dst, o);
+        }
+        if constexpr (SDPA_TRACE_DECODE) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            tr[6] = trace_clock();
+            trace_store(true);
         }
         return;
     }

@@ -263,7 +263,9 @@ FusedPlan fused_plan(const KernelSet* ks, int batch, int q_len, int kv_len_eff, 
 size_t fused_ws_bytes(const FusedPlan& f, int dv) {
     if (f.splits == 1) return 0;
     const size_t slots = (size_t)f.groups * f.splits * f.rv;
-    return kCounterBytes + align256(slots * dv * sizeof(float)) + align256(slots * 2 * sizeof(float));
+    // the timeline build appends one record per workgroup (decode_fused_kernel.h)
+    const size_t trace = SDPA_TRACE_DECODE ? align256((size_t)f.groups * f.splits * sdpa_dev::kTraceWords * 8) : 0;
+    return kCounterBytes + align256(slots * dv * sizeof(float)) + align256(slots * 2 * sizeof(float)) + trace;
 }
 
 // Byte extent of a strided tensor: [base, base + span).
