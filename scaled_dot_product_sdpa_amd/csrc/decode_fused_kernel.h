@@ -76,7 +76,13 @@ struct DfCfg {
     // 4 x 4 lanes (row, column quad) of one 16-byte write per row then cover the 64
     // banks instead of 4-way conflicting on 1 KB rows
     static constexpr int OP = DVP + (80 - DVP % 64) % 64;
-    static constexpr int LDS_M = NW * 16 * OP * 4 + 2 * NW * 16 * 4;  // per-wave O^T + (m, l) for the merge
+    // groups of up to RS rows keep the per-wave O^T beside the V blocks, so a wave
+    // writes it as soon as its keys are done; more rows reuse the V blocks' LDS
+    static constexpr int RS = 4;
+    static constexpr int LDS_OS = LDS_V + NW * RS * OP * 4;  // V blocks + separate O^T
+    static constexpr int LDS_OA = NW * 16 * OP * 4;          // O^T over the V blocks
+    static constexpr int ML_OFF = LDS_OS > LDS_OA ? LDS_OS : LDS_OA;  // per-wave (m, l)
+    static constexpr int LDS_M = ML_OFF + 2 * NW * 16 * 4;
     static constexpr int LDS_G = 16 * 32 * 4 + 2 * 16 * (DOW / 4) * 16;  // group merge: weights, half sums
     static constexpr int LDS_W = LDS_V > LDS_M ? (LDS_V > LDS_G ? LDS_V : LDS_G) : (LDS_M > LDS_G ? LDS_M : LDS_G);
     static constexpr int LDS = LDS_W;
@@ -351,25 +357,35 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
         }
 
         // ---- merge the waves through LDS: wave w's O^T, m, l of rows < RV ----
-        __syncthreads();  // every wave is done with its V block
+        // (up to RS rows: written beside the V blocks as soon as this wave is done;
+        // more: over the V blocks, once every wave is done with its block)
+        const bool sep = RV <= C::RS;
+        const int orw = sep ? C::RS : 16;  // O^T rows per wave in LDS
+        float* lo = reinterpret_cast<float*>(work + (sep ? C::LDS_V : 0));
+        float* lml = reinterpret_cast<float*>(work + C::ML_OFF);
+        auto put = [&]() __attribute__((always_inline)) {
+            if (r < RV) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    *reinterpret_cast<f32x4_t*>(lo + ((w * orw + r) * C::OP + 16 * db + 4 * g4)) = oacc[db];
+                if (g4 == 0) {
+                    lml[(w * 16 + r) * 2] = m_run;
+                    lml[(w * 16 + r) * 2 + 1] = l_row;
+                }
+            }
+        };
+        if (sep) put();
+        __syncthreads();  // every wave is done with its keys (and, up to RS rows, its partial is in LDS)
         if constexpr (SDPA_TRACE_DECODE) {
             if (tr[3] == 0) {
                 tr[3] = trace_clock();
                 tr[12] = trace_clock();
             }
         }
-        float* lo = reinterpret_cast<float*>(work);
-        float* lml = lo + NW * 16 * C::OP;
-        if (r < RV) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                *reinterpret_cast<f32x4_t*>(lo + ((w * 16 + r) * C::OP + 16 * db + 4 * g4)) = oacc[db];
-            if (g4 == 0) {
-                lml[(w * 16 + r) * 2] = m_run;
-                lml[(w * 16 + r) * 2 + 1] = l_row;
-            }
+        if (!sep) {
+            put();
+            __syncthreads();
         }
-        __syncthreads();
         if constexpr (SDPA_TRACE_DECODE) {
             if (tr[8] == 0) tr[8] = trace_clock();
         }
@@ -388,7 +404,7 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
                 const float mw = lml[(ww * 16 + row) * 2];
                 const float wt = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
                 l = __builtin_fmaf(wt, lml[(ww * 16 + row) * 2 + 1], l);
-                o += wt * *reinterpret_cast<const f32x4_t*>(lo + ((ww * 16 + row) * C::OP + c4));
+                o += wt * *reinterpret_cast<const f32x4_t*>(lo + ((ww * orw + row) * C::OP + c4));
             }
             if (direct) {
                 if (row < rows_g) {
