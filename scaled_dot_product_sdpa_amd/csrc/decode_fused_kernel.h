@@ -394,17 +394,25 @@ __global__ __launch_bounds__(C::NT) void decode_fused_kernel(const Params p, con
         const int nitems = RV * QPR;
         for (int it = tid; it < nitems; it += C::NT) {
             const int row = it / QPR, c4 = (it % QPR) * 4;
+            // every wave's (m, l) and O^T quad read at once (left to itself the compiler
+            // waited for each wave's read before issuing the next)
+            f32x2_t mlw[NW];
+            f32x4_t ow[NW];
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                mlw[ww] = *reinterpret_cast<const f32x2_t*>(lml + (ww * 16 + row) * 2);
+                ow[ww] = *reinterpret_cast<const f32x4_t*>(lo + ((ww * orw + row) * C::OP + c4));
+            }
             float M = NEG_INF;
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, lml[(ww * 16 + row) * 2]);
+            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mlw[ww][0]);
             f32x4_t o = {0.f, 0.f, 0.f, 0.f};
             float l = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) {
-                const float mw = lml[(ww * 16 + row) * 2];
-                const float wt = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
-                l = __builtin_fmaf(wt, lml[(ww * 16 + row) * 2 + 1], l);
-                o += wt * *reinterpret_cast<const f32x4_t*>(lo + ((ww * orw + row) * C::OP + c4));
+                const float wt = (mlw[ww][0] == NEG_INF) ? 0.f : fast_exp2(mlw[ww][0] - M);
+                l = __builtin_fmaf(wt, mlw[ww][1], l);
+                o += wt * ow[ww];
             }
             if (direct) {
                 if (row < rows_g) {
