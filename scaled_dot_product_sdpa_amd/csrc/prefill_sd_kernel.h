@@ -54,6 +54,10 @@ struct SdCfg {
     static constexpr int NI = BN * KC / (64 * NW);  // loads per wave per tile (K; V the same)
     static constexpr int XB = NS > 1 ? NW * NKB * 64 * 16 * 4 : 0;  // partial-score exchange
     static constexpr int LDS = 4 * TILEB + XB;
+    // the output tile staged in LDS (each wave's 32 rows x DH columns) where it fits, so
+    // that whole rows leave in 16-byte chunks, consecutive lanes on consecutive chunks
+    static constexpr int OPB = DH * 2 + 16;  // staged row pitch: 4 banks further per row
+    static constexpr bool STAGE_O = NW * 32 * OPB <= LDS;
     static constexpr int WPE = 2;          // waves per SIMD the registers must allow
     static_assert(NS == 1 || NS == 2, "head-dim split");
     static_assert(DH % 128 == 0 && KC <= 64 && 64 % KC == 0, "head dim");
@@ -433,7 +437,39 @@ __global__ __launch_bounds__(C::NT, C::WPE) void prefill_sd_kernel(const Params 
 
         // ---- epilogue: lane holds query col, columns DH hf + 32 db + 8 a4 + 4 hh .. +3 ----
         const float lsum_row = sum_x32(l_run);
-        if (rv) {
+        if constexpr (C::STAGE_O) {
+            // Through LDS: the 8-byte pieces above, written straight to memory, build
+            // each 128-byte line of a row from 8 store instructions (c5: 152-156 MB
+            // written per launch against 134 MB of output).  The wave's 32 rows x DH
+            // columns go to LDS (rows OPB bytes apart: the 32 rows of one write fall on
+            // 4-bank steps) and are read back a row pair per instruction, each lane
+            // storing one 16-byte chunk, consecutive lanes consecutive chunks.
+            constexpr int CPR = DH / 8;  // 16-byte chunks per row of the wave's share
+            const float inv = lsum_row > 0.f ? 1.f / lsum_row : 0.f;
+            __syncthreads();  // every wave is done with the K/V stages and the score exchange
+            char* const ob = smem + w * (32 * C::OPB);
+            char* const obw = ob + col * C::OPB + 8 * hh;
+    #pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+    #pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const u32x2_t x = {TR::pack(oacc[db][4 * a4] * inv, oacc[db][4 * a4 + 1] * inv),
+                                       TR::pack(oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv)};
+                    *reinterpret_cast<u32x2_t*>(obw + (4 * db + a4) * 16) = x;
+                }
+            __syncthreads();
+            const int c = lane % CPR, r0 = lane / CPR;  // this lane's chunk, first row
+            char* const obase = reinterpret_cast<char*>(p.o) +
+                                ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)(qmin + r0) * p.os[2]) * 2 +
+                                (DH * hf + 8 * c) * 2;
+            const int64_t ostep = (int64_t)p.os[2] * 2 * (64 / CPR);  // bytes between this lane's rows
+    #pragma unroll 1
+            for (int i = 0; i < 32 * CPR / 64; ++i) {
+                const int r = r0 + (64 / CPR) * i;
+                const u32x4_t y = *reinterpret_cast<const u32x4_t*>(ob + r * C::OPB + c * 16);
+                if (qmin + r < p.Lq) *reinterpret_cast<u32x4_t*>(obase + ostep * i) = y;
+            }
+        } else if (rv) {
             const float inv = lsum_row > 0.f ? 1.f / lsum_row : 0.f;
             char* orow = reinterpret_cast<char*>(p.o) +
                          ((int64_t)b * p.os[0] + (int64_t)qh * p.os[1] + (int64_t)qi * p.os[2]) * 2;
