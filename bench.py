@@ -276,11 +276,12 @@ TRACE_STAGES = (  # (record word, what the workgroup has done by then, last work
 )
 
 
-def timeline(name: str, calls: int, warmup: int, command: str) -> str:
+def timeline(name: str, calls: int, warmup: int, command: str, burst: int = 20) -> str:
     """In-kernel timeline of the single-launch decode kernel, from the timeline build of the library
     (libsdpa_trace.so): every workgroup records the constant 100 MHz clock at the stages of
-    TRACE_STAGES.  Each call runs on an idle GPU (a synchronize before and after); times are relative
-    to the first workgroup's start in the same call.  Returns a markdown summary."""
+    TRACE_STAGES.  Each sample is the last of `burst` calls launched back to back (the GPU busy, as
+    in a timed step); times are relative to the first workgroup's start in that call.  Returns a
+    markdown summary."""
     import re
     import statistics as stt
     import numpy as np
@@ -314,12 +315,28 @@ def timeline(name: str, calls: int, warmup: int, command: str) -> str:
         raise SystemExit(f"{name}: no timeline records in this library's workspace (is it the timeline build?)")
     recs, durs = [], []
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for i in range(warmup + calls):
+
+    def step(i):
         q, k, v, m = reps[i % nrep]
+        sdpa.forward(q, k, v, scale=c.scale, mask=m, mask_kind=c.mask_kind, out=out, workspace=ws)
+
+    for i in range(3):
+        step(i)
+    # `burst` calls back to back in one graph, replayed like a timed step; the last call's records are kept
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for i in range(burst):
+                step(i)
+    torch.cuda.current_stream().wait_stream(st)
+    for i in range(warmup + calls):
         ws[off:off + nwg * rb].zero_()
         torch.cuda.synchronize()
+        torch.cuda._sleep(COVER_CYCLES)
         e0.record()
-        sdpa.forward(q, k, v, scale=c.scale, mask=m, mask_kind=c.mask_kind, out=out, workspace=ws)
+        g.replay()
         e1.record()
         torch.cuda.synchronize()
         if i >= warmup:
@@ -327,7 +344,7 @@ def timeline(name: str, calls: int, warmup: int, command: str) -> str:
             if (r[:, 0] == 0).any() or (r[:, 5] == 0).any():
                 raise SystemExit("incomplete timeline records (a group recomputed off its XCD?)")
             recs.append(r)
-            durs.append(e0.elapsed_time(e1) * 1000)
+            durs.append(e0.elapsed_time(e1) * 1000 / burst)
     us = 0.01  # microseconds per tick of the 100 MHz clock
     per = {k: ([], []) for k, _, _ in TRACE_STAGES}
     segs = {n: [] for n in ("load", "keys", "store", "arrive", "merge", "span")}
@@ -359,9 +376,9 @@ def timeline(name: str, calls: int, warmup: int, command: str) -> str:
              "`SDPA_TRACE_DECODE=1`: each workgroup records the 100 MHz real-time clock at the stages below",
              "into the workspace; the product build has none of it):", "",
              "```", TRACE_BUILD, command, "```", "",
-             f"{calls} calls on cold K/V replicas, each on an idle GPU; times in µs from the first workgroup's",
-             "start in the same call, medians over the calls; 10 ns resolution.",
-             f"HIP-event time of one isolated call (host launch included): {med(durs):.2f} µs.", "",
+             f"{calls} samples on cold K/V replicas, each the last of {burst} calls replayed back to back from one",
+             "graph (as a timed step); times in µs from the first workgroup's start in that call, medians over the",
+             f"samples; 10 ns resolution. HIP-event time per call of a replay: {med(durs):.2f} µs.", "",
              "| stage | median workgroup | last workgroup |", "|---|---|---|"]
     for k, label, _ in TRACE_STAGES:
         lines.append(f"| {label} | {med(per[k][0]):.2f} | {med(per[k][1]):.2f} |")
