@@ -696,6 +696,67 @@ def ingest_counters(pmc_dir: str, calib_bytes: int):
     return out
 
 
+SQ_PASSES = (  # two rocprofv3 --pmc passes (8 SQ counters and GRBM_GUI_ACTIVE each)
+    ("p1", "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES "
+           "SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAIT_INST_LDS SQ_WAIT_ANY GRBM_GUI_ACTIVE"),
+    ("p2", "SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 "
+           "SQ_LDS_BANK_CONFLICT SQ_INST_LEVEL_LDS SQ_INSTS_LDS GRBM_GUI_ACTIVE"),
+)
+SQ_WORKLOADS = ("prefill-d72-none", "prefill-d72-causal", "prefill-d72-boolean", "prefill-d512-causal",
+                "prefill-d256-sliding-w1024")
+
+
+def ingest_sq(pmc_dir: str) -> str:
+    """Markdown table of SQ-counter figures for the prefill kernels, from <pmc_dir>/<W>_kt (kernel
+    trace), <W>_p1 and <W>_p2 (the SQ_PASSES) of `bench.py --profile-run --workload <W> --steps 3`."""
+    def files(sub, suffix):
+        return glob.glob(os.path.join(pmc_dir, sub, "**", f"*{suffix}.csv"), recursive=True)
+
+    rows = ["| workload | kernel | µs | clock GHz | MFMA busy | co-exec | VALU/MFMA | exp/MFMA | LDS/MFMA | "
+            "LDS bank-conflict cycles | waiting / ready / issuing |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for w in SQ_WORKLOADS:
+        kt = files(f"{w}_kt", "kernel_trace")
+        if not kt:
+            continue
+        durs = {}
+        for r in csv.DictReader(open(kt[0])):
+            if "prefill" in r["Kernel_Name"]:
+                durs.setdefault(_short(r["Kernel_Name"]), []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+        if not durs:
+            continue
+        kern = max(durs, key=lambda k: sum(durs[k]))
+        us = sum(durs[kern]) / len(durs[kern])
+        c = {}
+        for sub, _ in SQ_PASSES:
+            for f in files(f"{w}_{sub}", "counter_collection"):
+                per = {}
+                for r in csv.DictReader(open(f)):
+                    if _short(r["Kernel_Name"]) != kern:
+                        continue
+                    key = (r["Dispatch_Id"], r["Counter_Name"])
+                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+                names = set(n for _, n in per)
+                for n in names:
+                    vals = [v for (d, nn), v in per.items() if nn == n]
+                    c[n if n != "GRBM_GUI_ACTIVE" else f"GRBM_{sub}"] = sum(vals) / len(vals)
+        need = ("GRBM_p1", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+                "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY",
+                "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY")
+        if any(n not in c for n in need):
+            continue
+        cyc = c["GRBM_p1"] / 8.0  # GRBM_GUI_ACTIVE counts on every XCD
+        mf = c["SQ_INSTS_MFMA"]
+        wc = c["SQ_WAVE_CYCLES"]
+        rows.append(
+            f"| {w} | `{kern}` | {us:.1f} | {cyc / (us * 1e3):.2f} | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.1%} | "
+            f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.1%} | "
+            f"{(c['SQ_INSTS_VALU'] - mf) / mf:.2f} | {c['SQ_INSTS_VALU_TRANS_F32'] / mf:.2f} | "
+            f"{c['SQ_INSTS_LDS'] / mf:.2f} | {c['SQ_LDS_BANK_CONFLICT']:.3g} | "
+            f"{c['SQ_WAIT_ANY'] / wc:.0%} / {c['SQ_WAIT_INST_ANY'] / wc:.0%} / {c['SQ_ACTIVE_INST_ANY'] / wc:.0%} |")
+    return "\n".join(rows) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -714,12 +775,17 @@ def main():
                     help="print a markdown summary of a rocprofv3 kernel trace (no GPU needed)")
     ap.add_argument("--timeline", action="store_true",
                     help="in-kernel timeline of --workload's single-launch decode (needs libsdpa_trace.so)")
+    ap.add_argument("--ingest-sq", metavar="DIR",
+                    help="print the SQ-counter table of the prefill kernels from rocprofv3 output (no GPU needed)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("DIR", "COPY_MIB"),
                     help="write profiles/counters.json from rocprofv3 --pmc output (no GPU needed)")
     a = ap.parse_args()
 
     if a.summarize_trace:
         print(summarize_trace(a.summarize_trace[0], a.summarize_trace[1], a.steps if a.steps != 200 else 20))
+        return
+    if a.ingest_sq:
+        print(ingest_sq(a.ingest_sq), end="")
         return
     if a.ingest_counters:
         res = ingest_counters(a.ingest_counters[0], int(a.ingest_counters[1]) << 20)
