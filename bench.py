@@ -543,8 +543,11 @@ def _run_stats(kernels: dict, steps: int) -> dict:
         d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in last]
         st = [int(r["Start_Timestamp"]) for r in last]
         per = [(b - a) / 1000.0 for a, b in zip(st, st[1:])]
+        ds = sorted(d)
+        q = lambda f: ds[min(len(ds) - 1, int(round(f * (len(ds) - 1))))]
         res[(k, wg)] = {"workgroups": wg, "launches": len(rs), "timed": len(last), "avg_us": sum(d) / len(d),
-                  "period_us": (sum(per) / len(per)) if per else None}
+                        "p10_us": q(0.1), "median_us": q(0.5), "p90_us": q(0.9),
+                        "period_us": (sum(per) / len(per)) if per else None}
     return res
 
 
@@ -554,11 +557,12 @@ def summarize_trace(trace_csv: str, command: str, steps: int = 20) -> str:
     runs = trace_runs(trace_csv, steps)
     out = ["Command (repo root, one MI355X, `export TMPDIR=/tmp`):", "", "```", command, "```", "",
            f"Per workload, the library's kernels of the timed graph replay (the last {steps} launches of each "
-           "kernel in that workload's part of the trace): average kernel duration and average start-to-start "
-           "period of consecutive launches. A step of a two-kernel route is the sum of its kernels.", "",
-           "| workload | kernel | workgroups | launches (timed) | avg kernel us | avg period us | "
-           "work per launch | rate from avg kernel | of peak |",
-           "|---|---|---|---|---|---|---|---|---|"]
+           "kernel in that workload's part of the trace): average kernel duration, its p10 / median / p90 over "
+           "those launches, and the average start-to-start period of consecutive launches. A step of a "
+           "two-kernel route is the sum of its kernels.", "",
+           "| workload | kernel | workgroups | launches (timed) | avg kernel us | p10 / median / p90 us | "
+           "avg period us | work per launch | rate from avg kernel | of peak |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
     table = {}
     for name, ks in runs:
         tot = sum(v["avg_us"] for v in ks.values())
@@ -584,11 +588,12 @@ def summarize_trace(trace_csv: str, command: str, steps: int = 20) -> str:
         for (k, wg), v in sorted(ks.items(), key=lambda x: -x[1]["avg_us"]):
             rate, frac, _ = rate_of(v["avg_us"]) if len(ks) == 1 else ("", "", None)
             per = f"{v['period_us']:.2f}" if v["period_us"] is not None else "-"
-            out.append(f"| {name} | `{k}` | {wg} | {v['launches']} ({v['timed']}) | {v['avg_us']:.2f} | {per} | "
+            out.append(f"| {name} | `{k}` | {wg} | {v['launches']} ({v['timed']}) | {v['avg_us']:.2f} | "
+                       f"{v['p10_us']:.2f} / {v['median_us']:.2f} / {v['p90_us']:.2f} | {per} | "
                        f"{wstr} | {rate} | {frac} |")
         rate, frac, fv = rate_of(tot)
         if len(ks) > 1:
-            out.append(f"| {name} | step: the kernels above | | | {tot:.2f} | | {wstr} | {rate} | {frac} |")
+            out.append(f"| {name} | step: the kernels above | | | {tot:.2f} | | | {wstr} | {rate} | {frac} |")
         table[name] = {"kernels": {k: v for (k, _), v in ks.items()}, "step_kernel_us": tot,
                        "work_per_step": work_amt, "work_unit": unit, "frac_of_peak": fv}
     with open(os.path.join(ROOT, "profiles", "kernel_times.json"), "w") as f:
@@ -701,7 +706,9 @@ SQ_PASSES = (  # two rocprofv3 --pmc passes (8 SQ counters and GRBM_GUI_ACTIVE e
            "SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAIT_INST_LDS SQ_WAIT_ANY GRBM_GUI_ACTIVE"),
     ("p2", "SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 "
            "SQ_LDS_BANK_CONFLICT SQ_INST_LEVEL_LDS SQ_INSTS_LDS GRBM_GUI_ACTIVE"),
+    ("p3", "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE"),
 )
+MOPS_FLOPS = 512  # flops per unit of SQ_INSTS_VALU_MFMA_MOPS_* (checked against the instruction mix)
 SQ_WORKLOADS = ("prefill-d72-none", "prefill-d72-causal", "prefill-d72-boolean", "prefill-d512-causal",
                 "prefill-d256-sliding-w1024")
 
@@ -713,7 +720,8 @@ def ingest_sq(pmc_dir: str) -> str:
         return glob.glob(os.path.join(pmc_dir, sub, "**", f"*{suffix}.csv"), recursive=True)
 
     rows = ["| workload | kernel | µs | clock GHz | MFMA busy | co-exec | VALU/MFMA | exp/MFMA | LDS/MFMA | "
-            "LDS bank-conflict cycles | waiting / ready / issuing |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+            "LDS bank-conflict cycles | waiting / ready / issuing | matrix flops issued (counted) / algorithmic |",
+            "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for w in SQ_WORKLOADS:
         kt = files(f"{w}_kt", "kernel_trace")
         if not kt:
@@ -748,12 +756,17 @@ def ingest_sq(pmc_dir: str) -> str:
         cyc = c["GRBM_p1"] / 8.0  # GRBM_GUI_ACTIVE counts on every XCD
         mf = c["SQ_INSTS_MFMA"]
         wc = c["SQ_WAVE_CYCLES"]
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+        alg, _ = work(make_case(w))
+        issued = (f"{mops * MOPS_FLOPS / 1e9:.1f} GFLOP / {alg / 1e9:.1f} GFLOP = {mops * MOPS_FLOPS / alg:.3f}"
+                  if mops else "")
         rows.append(
             f"| {w} | `{kern}` | {us:.1f} | {cyc / (us * 1e3):.2f} | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.1%} | "
             f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.1%} | "
             f"{(c['SQ_INSTS_VALU'] - mf) / mf:.2f} | {c['SQ_INSTS_VALU_TRANS_F32'] / mf:.2f} | "
             f"{c['SQ_INSTS_LDS'] / mf:.2f} | {c['SQ_LDS_BANK_CONFLICT']:.3g} | "
-            f"{c['SQ_WAIT_ANY'] / wc:.0%} / {c['SQ_WAIT_INST_ANY'] / wc:.0%} / {c['SQ_ACTIVE_INST_ANY'] / wc:.0%} |")
+            f"{c['SQ_WAIT_ANY'] / wc:.0%} / {c['SQ_WAIT_INST_ANY'] / wc:.0%} / {c['SQ_ACTIVE_INST_ANY'] / wc:.0%} | "
+            f"{issued} |")
     return "\n".join(rows) + "\n"
 
 
