@@ -157,6 +157,23 @@ def test_output_canary_untouched(gpu_lib):
     assert_parity(out, oracle_out(c), "bf16", "canary")
 
 
+@pytest.mark.parametrize("D,mask_kind", [(512, "causal"), (512, "none"), (256, "causal"), (512, "boolean")])
+def test_wide_head_output_canary_with_ragged_rows(gpu_lib, D, mask_kind):
+    """The wide-head kernel stores whole rows (at D = 512 through an LDS-staged tile, a row pair
+    per instruction): rows past Lq in a ragged row tile must not be written, here the last head's
+    tail next to the canary."""
+    import scaled_dot_product_sdpa_amd as sdpa
+    c = si.make_case(1, 4, 2, 45, 77, D, dtype="bf16", mask_kind=mask_kind, seed=7, mask_shape="qk")
+    q, k, v, m = to_device(c)
+    n = 1 * 4 * 45 * D
+    buf = torch.full((4096 + n + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[4096:4096 + n].view(1, 4, 45, D)
+    sdpa.forward(q, k, v, scale=c.scale, mask=m, mask_kind=mask_kind, out=out)
+    torch.cuda.synchronize()
+    assert (buf[:4096] == 7.0).all() and (buf[-4096:] == 7.0).all()
+    assert_parity(out, oracle_out(c), "bf16", f"canary D={D} {mask_kind}")
+
+
 def test_unsupported_shapes_raise_not_fall_back(gpu_lib):
     import scaled_dot_product_sdpa_amd as sdpa
     q = torch.zeros(1, 2, 16, 48, dtype=torch.bfloat16, device="cuda")
